@@ -17,6 +17,9 @@ iterations in float64:
    distances; ties go to the lower j); replace each c_j by the float64 mean of
    its weights, the sum taken one element at a time in ascending column order
    and then divided by the count; a cluster with no weights keeps its c_j.
+   A centroid that is exactly zero is taken as +0 (at initialisation and
+   after each mean), so the sign of a zero never depends on sort or
+   summation order.
 3. Round: C_j = bf16(rn32(c_j)).
 4. Final assignment against the rounded C_j (ties to the lower j).
 5. Storage: indices 4 per byte, column 4b+i in bits 2i..2i+1; centroids as
@@ -59,7 +62,7 @@ def initial_centroids(w):
     k = w.shape[1]
     srt = np.sort(w, axis=1).astype(np.float64)
     idx = [((2 * j + 1) * k) // 8 for j in range(NCENT)]
-    return srt[:, idx]
+    return srt[:, idx] + 0.0          # -0.0 + 0.0 == +0.0
 
 
 def lloyd(w, iters=ITERS):
@@ -76,7 +79,7 @@ def lloyd(w, iters=ITERS):
             m = idx == j
             cnt = m.sum(axis=1)
             s = _sequential_sum(np.where(m, w64, 0.0))
-            new[:, j] = np.where(cnt > 0, s / np.maximum(cnt, 1), c[:, j])
+            new[:, j] = np.where(cnt > 0, s / np.maximum(cnt, 1) + 0.0, c[:, j])
         c = new
     return c, history
 

@@ -153,3 +153,12 @@ def test_lut2_index_packing_order():
     idx, cb = lut2.fit(w)
     assert np.array_equal(F.bf16_bits_to_f32(cb)[0], [0, 1, 2, 3])
     assert idx[0, 0] == (0 | 1 << 2 | 2 << 4 | 3 << 6)
+
+
+def test_lut2_zero_centroid_is_positive_zero():
+    # a quantile that lands on -0.0 and a cluster that stays empty keep +0
+    w = np.array([[-0.0] * 60 + [1.0, 2.0, 3.0, 4.0]], dtype=np.float32)
+    c = lut2.initial_centroids(w)
+    assert c[0, 0] == 0 and not np.signbit(c[0, 0])
+    idx, cb = lut2.fit(w)
+    assert not np.any(cb == 0x8000)
