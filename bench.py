@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized linear layer on one MI355X; prints ONE JSON line.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  prefill  the four Qwen3-8B-like layers at M = 8192 tokens, each
+           quantize_nvfp4(X bf16) -> gemm_w4a4(-> Y bf16)     (quantize is timed)
+  decode   the same four layer shapes, W4A16 (INT4 group-128) at M = 16
+  decode   the three Gemma3-12B-like layers, LUT2 at M = 8
+Inputs and packed weights are resident in HBM before the timed region.
+
+value = the step's algorithmic FLOPs / ms_per_step (TFLOP/s); the prefill
+FLOPs dominate (decode adds < 0.3 %).  ``parts`` breaks the step down with HIP
+events (torch.cuda.Event on the stream every kernel is launched on):
+per-layer quantize and GEMM times, the GEMM-only TFLOP/s as fractions of the
+fp16 (the dtype the MFMAs run), FP8 and FP4 dense peaks, and a separate
+decode sweep (all batch sizes) that rotates through > 512 MiB of weight copies
+so the 256 MiB Infinity Cache cannot serve repeats.
+
+``roofline`` describes the dominant kernel (gemm_w4a4); ``cpu_baseline`` times
+the CPU oracle (test infrastructure) on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "W4A4 prefill GEMM TFLOPS (% FP4 peak); W4A16 decode GB/s (% HBM) on 1 MI355X"
+PEAK = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # dense TFLOP/s
+HBM_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def _pct(v, lo=10, hi=90):
+    v = np.asarray(v, dtype=np.float64)
+    return float(np.median(v)), float(np.percentile(v, lo)), float(np.percentile(v, hi))
+
+
+def _traffic_record(kernel_src):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 --pmc
+    summary, if it was taken on the current kernel source (hash match)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_w4a4_qwen3_traffic.md")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    rec = {}
+    for line in open(path):
+        if line.startswith("traffic:"):
+            for kv in line.split()[1:]:
+                k, v = kv.split("=")
+                rec[k] = v
+    if rec.get("source_sha256_16") != h:
+        return None
+    return float(rec["bytes_per_step"])
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-reps", type=int, default=20)
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="rows of X per layer in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-sweep", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run the same kernels on its 1/N share of N; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_nvfp4_rtn_amd import qlin, synth, configs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ------------------------------------------------------------ set-up --
+    pre = configs.QWEN3_PREFILL
+    dec = configs.QWEN3_DECODE
+    lut = configs.GEMMA3_LUT2
+    M = pre.ms[0]
+    M_DEC, M_LUT = 16, 8
+
+    P = []   # prefill layers
+    for li, L in enumerate(pre.layers):
+        x = bf16(synth.activations_bf16(pre.cid, li, M, L.k, outliers=pre.outliers))
+        wc, ws, wt = qlin.quantize_nvfp4(f32(synth.weights(pre.cid, li, L.n, L.k)))
+        blob = qlin.repack_weights(qlin.QL_NVFP4, L.n, L.k, wc, ws, wt)
+        del wc, ws
+        P.append(dict(L=L, x=x, blob=blob,
+                      codes=torch.empty((M, L.k // 2), dtype=torch.uint8, device=dev),
+                      scales=torch.empty((M, L.k // 16), dtype=torch.uint8, device=dev),
+                      ts=torch.empty(1, dtype=torch.float32, device=dev),
+                      ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(M, L.k)),
+                                     dtype=torch.uint8, device=dev),
+                      y=torch.empty((M, L.n), dtype=torch.bfloat16, device=dev)))
+    D = []   # W4A16 decode layers
+    for li, L in enumerate(dec.layers):
+        c, s = qlin.quantize_int4_g128(f32(synth.weights(dec.cid, li, L.n, L.k)))
+        blob = qlin.repack_weights(qlin.QL_INT4_G128, L.n, L.k, c, s)
+        x32 = {m: bf16(synth.decode_x_bf16(dec.cid, li, m, L.k)) for m in dec.ms}
+        D.append(dict(L=L, blob=blob, x=x32,
+                      y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in dec.ms}))
+    U = []   # LUT2 decode layers
+    for li, L in enumerate(lut.layers):
+        i, c = qlin.fit_lut2(f32(synth.weights(lut.cid, li, L.n, L.k)))
+        blob = qlin.repack_weights(qlin.QL_LUT2, L.n, L.k, i, c)
+        xs = {m: bf16(synth.decode_x_bf16(lut.cid, li, m, L.k)) for m in lut.ms}
+        U.append(dict(L=L, blob=blob, x=xs,
+                      y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in lut.ms}))
+    torch.cuda.synchronize()
+
+    prefill_flops = sum(2.0 * M * p["L"].n * p["L"].k for p in P)
+    dec_flops = sum(2.0 * M_DEC * d["L"].n * d["L"].k for d in D)
+    lut_flops = sum(2.0 * M_LUT * u["L"].n * u["L"].k for u in U)
+    step_flops = prefill_flops + dec_flops + lut_flops
+
+    E = torch.cuda.Event
+
+    def step(ev=None):
+        for i, p in enumerate(P):
+            L = p["L"]
+            if ev is not None:
+                ev[i][0].record()
+            qlin.quantize_nvfp4(p["x"], codes=p["codes"], scales=p["scales"],
+                                workspace=p["ws"], ts_out=p["ts"])
+            if ev is not None:
+                ev[i][1].record()
+            qlin.gemm_w4a4(p["codes"], p["scales"], p["ts"], p["blob"], M, L.n, L.k, y=p["y"])
+            if ev is not None:
+                ev[i][2].record()
+        if ev is not None:
+            ev[len(P)][0].record()
+        for d in D:
+            qlin.gemm_w4a16(d["x"][M_DEC], d["blob"], d["L"].n, d["L"].k, y=d["y"][M_DEC])
+        for u in U:
+            qlin.gemm_lut2(u["x"][M_LUT], u["blob"], u["L"].n, u["L"].k, y=u["y"][M_LUT])
+        if ev is not None:
+            ev[len(P)][1].record()
+
+    # -------------------------------------------------- warm-up + timing --
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-kernel breakdown: a second, event-instrumented pass of the same steps
+    evs = [[[E(enable_timing=True) for _ in range(3)] for _ in range(len(P) + 1)]
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    q_ms = np.array([[evs[s][i][0].elapsed_time(evs[s][i][1]) for i in range(len(P))]
+                     for s in range(args.steps)])
+    g_ms = np.array([[evs[s][i][1].elapsed_time(evs[s][i][2]) for i in range(len(P))]
+                     for s in range(args.steps)])
+    d_ms = np.array([evs[s][len(P)][0].elapsed_time(evs[s][len(P)][1]) for s in range(args.steps)])
+
+    layers = []
+    for i, p in enumerate(P):
+        L = p["L"]
+        fl = 2.0 * M * L.n * L.k
+        gq = float(np.median(g_ms[:, i]))
+        qq = float(np.median(q_ms[:, i]))
+        qbytes = 2.0 * M * L.k + M * L.k / 2 + M * L.k / 16
+        layers.append({
+            "layer": L.name, "n": L.n, "k": L.k,
+            "gemm_us": round(gq * 1e3, 2), "gemm_tflops": round(fl / gq / 1e9, 1),
+            "quantize_us": round(qq * 1e3, 2),
+            "quantize_gbps_1pass_bytes": round(qbytes / qq / 1e6, 1),
+            "prefill_tflops_incl_quantize": round(fl / (gq + qq) / 1e9, 1),
+        })
+    gemm_ms_step = float(np.median(g_ms.sum(axis=1)))
+    quant_ms_step = float(np.median(q_ms.sum(axis=1)))
+    gemm_tflops = prefill_flops / gemm_ms_step / 1e9
+    prefill_tflops = prefill_flops / (gemm_ms_step + quant_ms_step) / 1e9
+
+    # --------------------------------------- decode sweep (MALL defeated) --
+    sweep = {}
+    if not args.no_decode_sweep:
+        def rotate(blobs_per_layer, nbytes_set):
+            copies = int(np.ceil(600e6 / nbytes_set))
+            return [[b.clone() for b in blobs_per_layer] for _ in range(copies)]
+        w_sets = rotate([d["blob"] for d in D], sum(d["blob"].numel() for d in D))
+        l_sets = rotate([u["blob"] for u in U], sum(u["blob"].numel() for u in U))
+        torch.cuda.synchronize()
+        combos = [("w4a16", li, m) for li in range(len(D)) for m in dec.ms] + \
+                 [("lut2", li, m) for li in range(len(U)) for m in lut.ms]
+        times = {c: [] for c in combos}
+        for rep in range(args.decode_reps + 3):
+            for c in combos:
+                kind, li, m = c
+                sets = w_sets if kind == "w4a16" else l_sets
+                rec = D[li] if kind == "w4a16" else U[li]
+                fn = qlin.gemm_w4a16 if kind == "w4a16" else qlin.gemm_lut2
+                a, b = E(enable_timing=True), E(enable_timing=True)
+                a.record()
+                for st in sets:
+                    fn(rec["x"][m], st[li], rec["L"].n, rec["L"].k, y=rec["y"][m])
+                b.record()
+                b.synchronize()
+                if rep >= 3:
+                    times[c].append(a.elapsed_time(b) / len(sets))
+        for c, t in times.items():
+            kind, li, m = c
+            L = (D[li] if kind == "w4a16" else U[li])["L"]
+            wbytes = (L.n * L.k / 2 + L.n * L.k / 64) if kind == "w4a16" else (L.n * L.k / 4 + 8 * L.n)
+            by = wbytes + 2.0 * m * L.k + 2.0 * m * L.n
+            med, p10, p90 = _pct(t)
+            sweep[f"{kind}/{L.name}/m{m}"] = {
+                "us": round(med * 1e3, 2), "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2),
+                "gbps": round(by / med / 1e6, 1), "hbm_frac": round(by / med / 1e6 / HBM_GBPS, 3)}
+        del w_sets, l_sets
+
+    def _agg(kind, ms):
+        out = {}
+        for m in ms:
+            vals = [v for k, v in sweep.items() if k.startswith(kind + "/") and k.endswith(f"/m{m}")]
+            if vals:
+                out[f"m{m}"] = round(float(np.mean([v["gbps"] for v in vals])), 1)
+        return out
+
+    # --------------------------------------------------- CPU baseline ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_rows, pre, M)
+
+    traffic = _traffic_record(os.path.join(ROOT, "decode_nvfp4_rtn_amd", "csrc", "gemm_w4a4.hip"))
+    out = {
+        "metric": METRIC,
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Qwen3-8B-like linear set: NVFP4 W4A4 prefill (quantize + GEMM, M=8192, "
+                        "bf16 out) over qkv/o/gate_up/down, + W4A16 decode M=16 over the same "
+                        "shapes, + Gemma3-12B-like LUT2 decode M=8",
+            "m_prefill": M, "m_w4a16": M_DEC, "m_lut2": M_LUT,
+            "prefill_layers_nk": [[p["L"].n, p["L"].k] for p in P],
+            "lut2_layers_nk": [[u["L"].n, u["L"].k] for u in U],
+        },
+        "roofline": {
+            "kernel": "gemm_w4a4",
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK["f16"],
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK["f16"], 4),
+            "traffic": traffic,
+            "per_launch": "2*M*N*K of the 4 layers / sum of their event-timed launch durations",
+        },
+        "cpu_baseline": cpu,
+        "parts": {
+            "prefill_tflops_incl_quantize": round(prefill_tflops, 1),
+            "gemm_w4a4_tflops": round(gemm_tflops, 1),
+            "gemm_w4a4_frac_fp4_peak": round(gemm_tflops / PEAK["fp4"], 4),
+            "gemm_w4a4_frac_fp8_peak": round(gemm_tflops / PEAK["fp8"], 4),
+            "gemm_w4a4_frac_f16_peak": round(gemm_tflops / PEAK["f16"], 4),
+            "quantize_ms_per_step": round(quant_ms_step, 4),
+            "gemm_ms_per_step": round(gemm_ms_step, 4),
+            "decode_block_ms_per_step": round(float(np.median(d_ms)), 4),
+            "layers": layers,
+            "w4a16_gbps_mean_over_layers": _agg("w4a16", dec.ms),
+            "lut2_gbps_mean_over_layers": _agg("lut2", lut.ms),
+            "decode_sweep": sweep,
+            "decode_timing": "events around back-to-back launches rotating over >600 MB of "
+                             "weight copies (Infinity Cache defeated); includes launch gaps",
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(rows, pre, M):
+    """The oracle as it stands, timed on the host on a bounded sample: for each
+    prefill layer, NVFP4-quantize `rows` rows of X (with the full tensor's
+    scale) and run the oracle's fp64 W4A4 product against the layer's weights
+    (weight quantization is offline, outside the timing, as on the GPU)."""
+    sys.path.insert(0, ROOT)
+    from oracle import nvfp4, gemm
+    from decode_nvfp4_rtn_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    prep = []
+    for li, L in enumerate(pre.layers):
+        xb = synth.activations_bf16(pre.cid, li, rows, L.k, outliers=pre.outliers)
+        w = synth.weights(pre.cid, li, L.n, L.k)
+        prep.append((L, synth.bf16_bits_as_f32(xb), nvfp4.quantize(w)))
+    t0 = time.perf_counter()
+    flops = 0.0
+    for L, x, wq in prep:
+        aq = nvfp4.quantize(x)
+        gemm.w4a4(*aq, *wq)
+        flops += 2.0 * rows * L.n * L.k
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of the {M} token rows of each of the 4 prefill layers "
+                      f"(quantize + fp64 product); {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

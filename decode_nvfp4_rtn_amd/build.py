@@ -1,0 +1,75 @@
+"""Build libqlin.so (hand-written HIP for gfx950) in-tree.
+
+    python -m decode_nvfp4_rtn_amd.build
+
+Each translation unit is compiled with hipcc for gfx950 only, then linked
+into ``decode_nvfp4_rtn_amd/libqlin.so``.  Flags:
+* ``-O3 -std=c++17 -fPIC``;
+* packed-fp32 instructions disabled for the device (the compiler may not
+  synthesise v_pk_{add,mul,fma}_f32);
+* no fast-math anywhere: divisions stay correctly rounded and denormals are
+  kept;
+* ``-ffp-contract=off`` for the quantizers, so no multiply is fused into an
+  add and every binary32 step rounds once.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libqlin.so")
+ARCH = "gfx950"
+
+SOURCES = {
+    "api.cpp": [],
+    "quantize.hip": ["-ffp-contract=off"],
+    "weight_prep.hip": ["-ffp-contract=off"],
+    "repack.hip": [],
+    "gemm_w4a4.hip": [],
+    "gemm_decode.hip": [],
+}
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def _compile(src, extra):
+    obj = os.path.join(BUILD, src + ".o")
+    cmd = [_hipcc(), *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose=True):
+    """Compile every source and link libqlin.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,246 @@
+// NVFP4 W4A4 prefill GEMM for gfx950 (CDNA4).
+//
+//   Y[m,n] = s_tA s_tW sum_g sA[m,g] sW[n,g] sum_{k in g} E2M1(a[m,k]) E2M1(w[n,k])
+//
+// Prefill runs both operands in NVFP4 (Mix-Quant technical summary,
+// gist.science, section 2, system-level deployment; Disaggregated
+// Quantization, format disaggregation).  Prefill is compute-bound because the
+// same weights serve every token (Disaggregated Quantization, opening
+// paragraph), so the contraction belongs on the matrix cores.
+//
+// Reconciling NVFP4 with gfx950.  gfx950's scaled MFMA applies power-of-two
+// (E8M0) scales per 32 k, while NVFP4 has E4M3 scales (4 significant bits)
+// per 16 k.  A dequantized element E2M1 * E4M3 needs up to 6 significant
+// bits, so it is NOT exact in FP8/FP6/FP4, but it IS exact in fp16 (11 bits;
+// the range 2^-10 .. 2688 is all normal).  This kernel therefore
+//   1. converts each 4-bit code to fp16 with the hardware converter
+//      (v_cvt_scalef32_pk_f16_fp4, scale 1.0: two codes per instruction),
+//   2. multiplies by the group scale with v_pk_mul_f16 (exact product),
+//   3. runs v_mfma_f32_16x16x32_f16 with fp32 accumulation,
+//   4. multiplies by s_tA * s_tW in the epilogue.
+// Products of dequantized operands are exact in fp32; only the accumulation
+// rounds.  The ceiling of this exact formulation is the dense fp16 MFMA rate.
+//
+// Tiling.  Block tile 128 (n) x 128 (m), k-step 128, four waves in 2 x 2,
+// each wave 64 x 64 = 4 x 4 MFMA tiles.  Codes and scales of both operands are
+// staged through LDS (double buffered, one barrier per k-step) in their
+// packed 4-bit form, so LDS traffic is a quarter of an fp16 GEMM's; every wave
+// dequantizes its own fragments in registers.  MFMA operand k-mapping: lane
+// (r = l%16, q = l/16) holds groups 2q and 2q+1 of the k-step (16 contiguous
+// code bytes, one 16-byte LDS read), and MFMA (c, s) (c, s in {0,1}) uses the
+// 8 codes of group 2q+c, half s.  Both operands use the same mapping, so the
+// sum over k is unchanged.  Weights are the A operand (16 n-rows) and
+// activations the B operand, so each lane owns 4 consecutive n of one m in
+// the output and stores them with one vector store.
+//
+// Block order: tiles are grouped 8 m-tiles wide for L2 reuse, and block ids
+// are remapped so that consecutive tiles land on the same XCD (the hardware
+// deals workgroups round-robin over the 8 XCDs, each with its own L2).
+#include "qlin_internal.hpp"
+
+namespace qlin {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128;
+constexpr int RS = 80;             // LDS row stride in bytes (64 data + 16 pad)
+constexpr int kThreads = 256;
+constexpr int GROUP_M = 8;
+
+struct __attribute__((aligned(16))) Smem {
+  uint8_t wc[2][BN * RS];
+  uint8_t xc[2][BM * RS];
+  uint8_t ws[2][BN * 8];
+  uint8_t xs[2][BM * 8];
+};
+
+__device__ __forceinline__ half2_t h2(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
+// 8 E2M1 codes (low nibble first) times an fp16 group scale -> 8 exact fp16.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s) {
+  half2_t a = h2(w, 0) * s, b = h2(w, 1) * s, c = h2(w, 2) * s, d = h2(w, 3) * s;
+  return half8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E4M3 byte `sel` of `w` as an fp16 pair (exact: E4M3 values are fp16 values).
+__device__ __forceinline__ half2_t scale2(uint32_t w, int sel) {
+  float f = sel == 0 ? __builtin_amdgcn_cvt_f32_fp8(w, 0) : __builtin_amdgcn_cvt_f32_fp8(w, 1);
+  _Float16 h = static_cast<_Float16>(f);
+  return half2_t{h, h};
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <bool kBF16Out>
+__global__ __launch_bounds__(kThreads, 2) void w4a4_kernel(
+    const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
+    const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
+    int64_t ws_off, int M, int N, int K, void* __restrict__ y) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+
+  // XCD-aware remap, then GROUP_M-wide grouped order
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (t / in_group) * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (t % in_group) % gsz;
+  const int tn = (t % in_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int KT = K / 128;
+  const int NT16 = N / 16;
+  const int wn = wave & 1, wm = wave >> 1;
+  const uint8_t* wcodes = blob + wc_off;
+  const uint8_t* wscales = blob + ws_off;
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 pw[2], px[2];
+  uint2 ps;
+  auto gload = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = i * kThreads + tid;
+      const int nt = tn * 8 + (u >> 6);
+      pw[i] = nt < NT16 ? *reinterpret_cast<const uint4*>(
+                              wcodes + (int64_t(nt) * KT + ks) * 1024 + (u & 63) * 16)
+                        : make_uint4(0, 0, 0, 0);
+      const int m = m0 + (u >> 2);
+      px[i] = m < M ? *reinterpret_cast<const uint4*>(xcodes + int64_t(m) * (K / 2) + ks * 64 +
+                                                      (u & 3) * 16)
+                    : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < 128) {
+      const int nt = tn * 8 + (tid >> 4);
+      ps = nt < NT16 ? *reinterpret_cast<const uint2*>(
+                           wscales + (int64_t(nt) * KT + ks) * 128 + (tid & 15) * 8)
+                     : make_uint2(0, 0);
+    } else {
+      const int m = m0 + tid - 128;
+      ps = m < M ? *reinterpret_cast<const uint2*>(xscales + int64_t(m) * (K / 16) + ks * 8)
+                 : make_uint2(0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = i * kThreads + tid;
+      const int wr = (u >> 6) * 16 + ((u & 63) >> 2);
+      *reinterpret_cast<uint4*>(&sm.wc[buf][wr * RS + (u & 3) * 16]) = pw[i];
+      *reinterpret_cast<uint4*>(&sm.xc[buf][(u >> 2) * RS + (u & 3) * 16]) = px[i];
+    }
+    if (tid < 128)
+      *reinterpret_cast<uint2*>(&sm.ws[buf][tid * 8]) = ps;
+    else
+      *reinterpret_cast<uint2*>(&sm.xs[buf][(tid - 128) * 8]) = ps;
+  };
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+
+  const int r = lane & 15, q = lane >> 4;
+  for (int ks = 0; ks < KT; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < KT) gload(ks + 1);
+
+    uint4 wraw[4], xraw[4];
+    uint32_t wsc[4], xsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wn * 64 + i * 16 + r;
+      wraw[i] = *reinterpret_cast<const uint4*>(&sm.wc[buf][row * RS + q * 16]);
+      wsc[i] = *reinterpret_cast<const uint16_t*>(&sm.ws[buf][row * 8 + 2 * q]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wm * 64 + j * 16 + r;
+      xraw[j] = *reinterpret_cast<const uint4*>(&sm.xc[buf][row * RS + q * 16]);
+      xsc[j] = *reinterpret_cast<const uint16_t*>(&sm.xs[buf][row * 8 + 2 * q]);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {          // d = 2c + s
+      half8_t wf[4], xf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = d == 0 ? wraw[i].x : d == 1 ? wraw[i].y : d == 2 ? wraw[i].z : wraw[i].w;
+        wf[i] = dequant8(w, scale2(wsc[i], d >> 1));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = d == 0 ? xraw[j].x : d == 1 ? xraw[j].y : d == 2 ? xraw[j].z : xraw[j].w;
+        xf[j] = dequant8(w, scale2(xsc[j], d >> 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    }
+
+    if (ks + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: scale by s_tA * s_tW and store 4 consecutive n per lane
+  const float st = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + wn * 64 + i * 16 + 4 * q;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + wm * 64 + j * 16 + r;
+      if (m >= M) continue;
+      const floatx4 v = acc[i][j] * st;
+      if (kBF16Out) {
+        uint2 o;
+        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                            const void* w_packed, int64_t m, int64_t n, int64_t k, void* y,
+                            int y_dtype, hipStream_t s) {
+  const BlobLayout L = blob_layout(0, n, k);
+  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+  const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
+  if (y_dtype == 1)
+    w4a4_kernel<true><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob, L.codes_off,
+                                                 L.aux_off, int(m), int(n), int(k), y);
+  else
+    w4a4_kernel<false><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob, L.codes_off,
+                                                  L.aux_off, int(m), int(n), int(k), y);
+  return hipGetLastError();
+}
+
+}  // namespace qlin

@@ -1,0 +1,98 @@
+// Internal declarations shared by the libqlin.so translation units.
+// Not part of the public ABI (include/qlin.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace qlin {
+
+// Streaming (non-temporal) vector loads: data read once should not displace
+// reused data in the caches.
+typedef uint32_t qlin_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t qlin_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  qlin_u32x4 v = __builtin_nontemporal_load(static_cast<const qlin_u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 load_nt8(const void* p) {
+  qlin_u32x2 v = __builtin_nontemporal_load(static_cast<const qlin_u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Packed weight blob: a 256-byte header followed by the data regions.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBlobMagic = 0x4E494C51u;  // "QLIN"
+constexpr int kBlobVersion = 1;
+constexpr size_t kHeaderBytes = 256;
+
+struct BlobHeader {
+  uint32_t magic;
+  int32_t version;
+  int32_t fmt;
+  int32_t reserved;
+  int64_t n;
+  int64_t k;
+  float tensor_scale;  // NVFP4 only
+  uint32_t pad[(256 - 36) / 4];
+};
+static_assert(sizeof(BlobHeader) == 256, "header size");
+
+// Region offsets (bytes from the start of the blob), shared by the repacker
+// and the GEMM launchers.
+struct BlobLayout {
+  size_t codes_off, codes_bytes;
+  size_t aux_off, aux_bytes;  // scales or codebook
+  size_t total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline BlobLayout blob_layout(int fmt, int64_t n, int64_t k) {
+  BlobLayout L{};
+  L.codes_off = kHeaderBytes;
+  if (fmt == 0) {          // NVFP4: codes n*k/2, E4M3 scales n*k/16
+    L.codes_bytes = size_t(n) * k / 2;
+    L.aux_bytes = size_t(n) * k / 16;
+  } else if (fmt == 1) {   // INT4 g128: codes n*k/2, bf16 scales n*k/128*2
+    L.codes_bytes = size_t(n) * k / 2;
+    L.aux_bytes = size_t(n) * (k / 128) * 2;
+  } else {                 // LUT2: indices n*k/4, codebook 8 bytes per row
+    L.codes_bytes = size_t(n) * k / 4;
+    L.aux_bytes = size_t(n) * 8;
+  }
+  L.aux_off = align256(L.codes_off + L.codes_bytes);
+  L.total = align256(L.aux_off + L.aux_bytes);
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files).  They assume validated arguments
+// and return the hipError_t of the launch.
+// ---------------------------------------------------------------------------
+int quantize_blocks(int64_t rows, int64_t cols);
+hipError_t launch_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                 uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                 bool static_scale, uint32_t* partial, hipStream_t s);
+
+hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* codes,
+                                uint16_t* scales, hipStream_t s);
+size_t lut2_workspace(int64_t n, int64_t k);
+hipError_t launch_fit_lut2(const float* w, int64_t n, int64_t k, uint8_t* idx,
+                           uint16_t* centroids, void* ws, hipStream_t s);
+
+hipError_t launch_repack(int fmt, int64_t n, int64_t k, const uint8_t* codes,
+                         const void* aux, const float* tensor_scale, void* packed,
+                         hipStream_t s);
+
+hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const float* a_ts, const void* w_packed, int64_t m, int64_t n,
+                            int64_t k, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n,
+                             int64_t k, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_lut2(const void* x, const void* w_packed, int64_t m, int64_t n,
+                            int64_t k, void* y, int y_dtype, hipStream_t s);
+
+}  // namespace qlin

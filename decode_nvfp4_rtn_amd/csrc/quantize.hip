@@ -1,0 +1,226 @@
+// NVFP4 activation / weight quantizer for gfx950, two passes.
+//
+// Method: NVFP4 with one E4M3 scale per 16-element group plus an fp32
+// tensor scale, quantized by plain round-to-nearest (Mix-Quant technical
+// summary, gist.science, section 2 "Method", hybrid-precision strategy).
+// Element format E2M1 and scale format E4M3 follow the OCP MX v1.0 and OFP8
+// specifications.  The binary32 operation order is fixed by include/qlin.h.
+//
+// Pass 1 (amax): every block reduces max|x| over a grid-strided slice with
+//   wavefront shuffles and writes one partial maximum (as the bit pattern of
+//   a non-negative float, which orders like an unsigned integer).
+// Pass 2 (encode): every block first folds the partial maxima (a few KiB,
+//   L2-resident) into amax and s_t -- so no third launch and no atomics are
+//   needed and the result is deterministic -- then each thread encodes whole
+//   16-element groups: one 32 B (bf16) or 64 B (fp32) load, one 8 B code
+//   store and one scale byte per group.  Both passes are HBM-bound streams.
+//
+// This translation unit is compiled without fast-math and with
+// -ffp-contract=off: every division is the correctly rounded binary32
+// division and no multiply is fused into an add.
+#include "qlin_internal.hpp"
+
+namespace qlin {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 1024;
+constexpr int kMaxEncodeBlocks = 4096;
+
+// |x| as a binary32 bit pattern, for the two input dtypes.
+__device__ __forceinline__ uint32_t abs_bits_bf16_pair(uint32_t w, uint32_t cur) {
+  uint32_t lo = (w & 0x7FFFu) << 16;
+  uint32_t hi = w & 0x7FFF0000u;
+  cur = cur > lo ? cur : lo;
+  return cur > hi ? cur : hi;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t sh[kThreads / 64];
+  v = wave_max_u32(v);
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wid] = v;
+  __syncthreads();
+  uint32_t r = sh[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = r > sh[i] ? r : sh[i];
+  __syncthreads();
+  return r;
+}
+
+// Pass 1: partial[blockIdx.x] = max |x| over this block's grid-strided chunks
+// of 16 bytes.  `nvec` counts 16-byte vectors of the whole tensor.
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x, int64_t nvec,
+                                                        uint32_t* __restrict__ partial) {
+  uint32_t m = 0;
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
+    uint4 v = load_nt16(&x[i]);
+    if (kBF16) {
+      m = abs_bits_bf16_pair(v.x, m);
+      m = abs_bits_bf16_pair(v.y, m);
+      m = abs_bits_bf16_pair(v.z, m);
+      m = abs_bits_bf16_pair(v.w, m);
+    } else {
+      uint32_t a = v.x & 0x7FFFFFFFu, b = v.y & 0x7FFFFFFFu;
+      uint32_t c = v.z & 0x7FFFFFFFu, d = v.w & 0x7FFFFFFFu;
+      a = a > b ? a : b;
+      c = c > d ? c : d;
+      a = a > c ? a : c;
+      m = m > a ? m : a;
+    }
+  }
+  m = block_max_u32(m);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// E4M3 (OCP E4M3FN) encoding of a non-negative binary32 value: round to
+// nearest, ties to even, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t enc_e4m3(float q) {
+  if (!(q < 448.0f)) return 0x7Eu;
+  if (q < 0.015625f) {                      // below 2^-6: subnormal quantum 2^-9
+    return static_cast<uint32_t>(__builtin_rintf(q * 512.0f));  // 0..8 (8 == 2^-6)
+  }
+  uint32_t u = __float_as_uint(q);
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // round mantissa to 3 bits, RNE
+  r &= 0xFFF00000u;
+  uint32_t e = (r >> 23) - 120u;                // biased E4M3 exponent (1..15)
+  uint32_t code = (e << 3) | ((r >> 20) & 7u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Exact binary32 value of a non-negative E4M3 code (0..0x7E).
+__device__ __forceinline__ float dec_e4m3(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return static_cast<float>(m) * 0.001953125f;  // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 code of a binary32 value: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the
+// even code, saturating at 6; the sign bit is copied.
+__device__ __forceinline__ uint32_t enc_e2m1(float y) {
+  float a = __builtin_fabsf(y);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+template <bool kBF16>
+__device__ __forceinline__ void load_group(const void* x, int64_t g, float v[16]) {
+  if (kBF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * g;
+    uint4 a = load_nt16(p), b = load_nt16(p + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(x) + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 t = load_nt16(p + i);
+      v[4 * i] = __uint_as_float(t.x);
+      v[4 * i + 1] = __uint_as_float(t.y);
+      v[4 * i + 2] = __uint_as_float(t.z);
+      v[4 * i + 3] = __uint_as_float(t.w);
+    }
+  }
+}
+
+// Pass 2: tensor scale, then group scales and element codes.
+template <bool kBF16>
+__global__ __launch_bounds__(kThreads) void encode_kernel(
+    const void* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int static_scale,
+    const uint32_t* __restrict__ partial, int npartial) {
+  float s_t;
+  if (static_scale) {
+    s_t = *tensor_scale;
+  } else {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < npartial; i += kThreads) m = m > partial[i] ? m : partial[i];
+    m = block_max_u32(m);
+    s_t = __uint_as_float(m) / 2688.0f;  // 2688 = 6 * 448
+    if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  }
+  const float d = 6.0f * s_t;
+
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  for (int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
+    float v[16];
+    load_group<kBF16>(x, g, v);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+    uint32_t sc = (d == 0.0f) ? 0u : enc_e4m3(a / d);
+    const float p = dec_e4m3(sc) * s_t;
+    uint32_t w0 = 0, w1 = 0;
+    if (p == 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w0 |= ((__float_as_uint(v[i]) >> 31) << 3) << (4 * i);
+        w1 |= ((__float_as_uint(v[8 + i]) >> 31) << 3) << (4 * i);
+      }
+    } else {
+      const float inv = 1.0f / p;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        w0 |= enc_e2m1(v[i] * inv) << (4 * i);
+        w1 |= enc_e2m1(v[8 + i] * inv) << (4 * i);
+      }
+    }
+    reinterpret_cast<uint2*>(codes)[g] = make_uint2(w0, w1);
+    scales[g] = static_cast<uint8_t>(sc);
+  }
+}
+
+}  // namespace
+
+int quantize_blocks(int64_t rows, int64_t cols) {
+  const int64_t vec = rows * cols / 8;  // 16-byte vectors of a bf16 tensor
+  int64_t b = (vec + kThreads * 4 - 1) / (kThreads * 4);
+  if (b < 1) b = 1;
+  if (b > kMaxPartials) b = kMaxPartials;
+  return static_cast<int>(b);
+}
+
+hipError_t launch_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                 uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                 bool static_scale, uint32_t* partial, hipStream_t s) {
+  const bool bf16 = x_dtype == 1;
+  const int64_t total = rows * cols;
+  const int npart = quantize_blocks(rows, cols);
+  if (!static_scale) {
+    const int64_t nvec = bf16 ? total / 8 : total / 4;
+    if (bf16)
+      amax_kernel<true><<<npart, kThreads, 0, s>>>(static_cast<const uint4*>(x), nvec, partial);
+    else
+      amax_kernel<false><<<npart, kThreads, 0, s>>>(static_cast<const uint4*>(x), nvec, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t ngroups = total / 16;
+  int64_t blocks = (ngroups + kThreads - 1) / kThreads;
+  if (blocks > kMaxEncodeBlocks) blocks = kMaxEncodeBlocks;
+  if (bf16)
+    encode_kernel<true><<<static_cast<int>(blocks), kThreads, 0, s>>>(
+        x, ngroups, codes, scales, tensor_scale, static_scale, partial, npart);
+  else
+    encode_kernel<false><<<static_cast<int>(blocks), kThreads, 0, s>>>(
+        x, ngroups, codes, scales, tensor_scale, static_scale, partial, npart);
+  return hipGetLastError();
+}
+
+}  // namespace qlin

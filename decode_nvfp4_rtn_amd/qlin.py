@@ -1,0 +1,218 @@
+"""Thin Python binding over libqlin.so (include/qlin.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libqlin.so.  torch supplies device memory and the current stream.
+Importing this module loads the library and raises ImportError when it has
+not been built (``python -m decode_nvfp4_rtn_amd.build``); there is no
+fallback implementation.
+
+Function names match the C entry points.  Tensors must be contiguous and on
+the GPU; outputs are allocated with torch unless passed in.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlin.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decode_nvfp4_rtn_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+QL_OK, QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EDTYPE, QL_EWORKSPACE, QL_EHIP, QL_EFORMAT = range(8)
+QL_F32, QL_BF16 = 0, 1
+QL_NVFP4, QL_INT4_G128, QL_LUT2 = 0, 1, 2
+QL_STATIC_SCALE = 1
+
+_vp, _i64, _sz, _int, _uint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
+
+_SIGS = {
+    "ql_status_str": (ctypes.c_char_p, [_int]),
+    "ql_version": (_int, []),
+    "quantize_nvfp4_workspace": (_sz, [_i64, _i64]),
+    "quantize_nvfp4": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _uint, _vp, _sz, _vp]),
+    "quantize_int4_g128": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "fit_lut2_workspace": (_sz, [_i64, _i64]),
+    "fit_lut2": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "repack_weights_bytes": (_sz, [_int, _i64, _i64]),
+    "repack_weights": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "gemm_w4a4": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "gemm_w4a16": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "gemm_lut2": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class QlinError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {_lib.ql_status_str(status).decode()} (status {status})")
+
+
+def _check(fn, status):
+    if status != QL_OK:
+        raise QlinError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def ql_status_str(status):
+    return _lib.ql_status_str(status).decode()
+
+
+def ql_version():
+    return _lib.ql_version()
+
+
+def quantize_nvfp4_workspace(rows, cols):
+    return _lib.quantize_nvfp4_workspace(rows, cols)
+
+
+def quantize_nvfp4(x, tensor_scale=None, codes=None, scales=None, workspace=None, stream=None,
+                   ts_out=None):
+    """NVFP4 round-to-nearest quantization of x [rows, cols] (fp32 or bf16).
+
+    tensor_scale: None computes s_t from max|x| (written to ts_out, a 1-element
+    fp32 GPU tensor, allocated when not given); a 1-element fp32 GPU tensor
+    holding a calibrated s_t is used as is (QL_STATIC_SCALE).
+    Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], s_t fp32 [1]).
+    """
+    _dev(x, "x")
+    rows, cols = x.shape
+    dt = {torch.float32: QL_F32, torch.bfloat16: QL_BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be float32 or bfloat16")
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    flags = 0
+    if tensor_scale is None:
+        ts = ts_out if ts_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        ts = _dev(tensor_scale, "tensor_scale")
+        flags = QL_STATIC_SCALE
+    wsb = _lib.quantize_nvfp4_workspace(rows, cols)
+    if workspace is None and not flags:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _check("quantize_nvfp4", _lib.quantize_nvfp4(
+        _ptr(x), dt, rows, cols, _ptr(codes), _ptr(scales), _ptr(ts), flags,
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return codes, scales, ts
+
+
+def quantize_int4_g128(w, codes=None, scales=None, stream=None):
+    """Symmetric INT4 group-128 quantization of fp32 weights [n, k].
+    Returns (codes uint8 [n, k/2], scales int16 (bf16 bits) [n, k/128])."""
+    _dev(w, "w")
+    n, k = w.shape
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // 128), dtype=torch.int16, device=w.device)
+    _check("quantize_int4_g128", _lib.quantize_int4_g128(
+        _ptr(w), n, k, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def fit_lut2_workspace(n, k):
+    return _lib.fit_lut2_workspace(n, k)
+
+
+def fit_lut2(w, idx=None, centroids=None, workspace=None, stream=None):
+    """2-bit codebook fit of fp32 weights [n, k] (10 Lloyd iterations per row).
+    Returns (idx uint8 [n, k/4], centroids int16 (bf16 bits) [n, 4])."""
+    _dev(w, "w")
+    n, k = w.shape
+    if idx is None:
+        idx = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    if centroids is None:
+        centroids = torch.empty((n, 4), dtype=torch.int16, device=w.device)
+    wsb = _lib.fit_lut2_workspace(n, k)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=w.device)
+    _check("fit_lut2", _lib.fit_lut2(_ptr(w), n, k, _ptr(idx), _ptr(centroids), _ptr(workspace),
+                                     workspace.numel(), _stream(stream)))
+    return idx, centroids
+
+
+def repack_weights_bytes(fmt, n, k):
+    return _lib.repack_weights_bytes(fmt, n, k)
+
+
+def repack_weights(fmt, n, k, codes, scales_or_lut, tensor_scale=None, packed=None, stream=None):
+    """Repack canonical quantized weights into the kernel operand order.
+    Returns the packed blob (uint8 GPU tensor)."""
+    nbytes = _lib.repack_weights_bytes(fmt, n, k)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check("repack_weights", _lib.repack_weights(
+        fmt, n, k, _ptr(codes), _ptr(scales_or_lut), _ptr(tensor_scale), _ptr(packed),
+        packed.numel(), _stream(stream)))
+    return packed
+
+
+def _out(y, m, n, dtype, dev):
+    if y is None:
+        y = torch.empty((m, n), dtype=dtype, device=dev)
+    dt = {torch.float32: QL_F32, torch.bfloat16: QL_BF16}.get(y.dtype)
+    if dt is None:
+        raise ValueError("y must be float32 or bfloat16")
+    return y, dt
+
+
+def gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k, y=None,
+              out_dtype=torch.float32, stream=None):
+    """NVFP4 W4A4 prefill GEMM: Y [m, n] = dequant(A) dequant(W)^T."""
+    y, dt = _out(y, m, n, out_dtype, a_codes.device)
+    _check("gemm_w4a4", _lib.gemm_w4a4(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(w_packed), m, n, k, _ptr(y),
+        dt, _stream(stream)))
+    return y
+
+
+def gemm_w4a16(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
+    """W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times INT4-g128 weights^T."""
+    _dev(x, "x")
+    m = x.shape[0]
+    y, dt = _out(y, m, n, out_dtype, x.device)
+    _check("gemm_w4a16", _lib.gemm_w4a16(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
+                                         _stream(stream)))
+    return y
+
+
+def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
+    """LUT2 decode GEMM: Y [m, n] = X bf16 [m, k] times codebook weights^T."""
+    _dev(x, "x")
+    m = x.shape[0]
+    y, dt = _out(y, m, n, out_dtype, x.device)
+    _check("gemm_lut2", _lib.gemm_lut2(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
+                                       _stream(stream)))
+    return y
+
+
+def raw():
+    """The ctypes handle of libqlin.so (for tests that call the C ABI directly)."""
+    return _lib

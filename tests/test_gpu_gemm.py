@@ -1,0 +1,261 @@
+"""GPU parity of the three GEMMs against the oracle's fp64 products.
+
+Bar: max |y - y_ref| / rms(y_ref) <= 1e-3 for fp32 outputs; for bf16 outputs
+the per-element rule of oracle.gemm.bf16_output_ok.  The oracle quantizes its
+own operands from the same seeded inputs (bit-equality of those codes with the
+GPU's is checked in test_gpu_quantize.py); at full size it computes the
+outputs of a seeded sample of rows and columns, one by one, in the launch
+configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from decode_nvfp4_rtn_amd import synth, configs
+from oracle import nvfp4, int4, lut2, gemm
+from tests.gpu_common import (require_gpu, say, dev_f32, dev_bf16, host_f64, sample_rows)
+
+pytestmark = pytest.mark.gpu
+TOL = gemm.TOL
+
+
+# ------------------------------------------------------------- helpers --
+
+def _nvfp4_blob(q, w):
+    wc, ws, wt = q.quantize_nvfp4(dev_f32(w))
+    n, k = w.shape
+    return q.repack_weights(q.QL_NVFP4, n, k, wc, ws, wt)
+
+
+def _int4_blob(q, w):
+    c, s = q.quantize_int4_g128(dev_f32(w))
+    n, k = w.shape
+    return q.repack_weights(q.QL_INT4_G128, n, k, c, s)
+
+
+def _lut2_blob(q, w):
+    i, c = q.fit_lut2(dev_f32(w))
+    n, k = w.shape
+    return q.repack_weights(q.QL_LUT2, n, k, i, c)
+
+
+def _check(y_gpu, y_ref, bf16):
+    if bf16:
+        assert gemm.bf16_output_ok(y_gpu, y_ref), gemm.normalized_max_error(y_gpu, y_ref)
+    else:
+        e = gemm.normalized_max_error(y_gpu, y_ref)
+        assert e <= TOL, e
+
+
+# ---------------------------------------------------------------- W4A4 --
+
+def test_w4a4_tiny_full():
+    q = require_gpu()
+    x = synth.activations(1, 0, 64, 512, outliers="channels")
+    w = synth.weights(1, 0, 256, 512)
+    say("w4a4 tiny 64x256x512")
+    blob = _nvfp4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_f32(x))
+    y = q.gemm_w4a4(ac, as_, at, blob, 64, 256, 512, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = gemm.w4a4(*nvfp4.quantize(x), *nvfp4.quantize(w))
+    _check(host_f64(y), ref, False)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 48, 256), (130, 272, 384), (257, 128, 1024)])
+def test_w4a4_ragged(m, n, k):
+    q = require_gpu()
+    x = synth.activations(8, m, m, k, outliers="channels")
+    w = synth.weights(8, n, n, k)
+    say("w4a4 ragged", m, n, k)
+    blob = _nvfp4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_f32(x))
+    for dt in (torch.float32, torch.bfloat16):
+        y = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=dt)
+        torch.cuda.synchronize()
+        ref = gemm.w4a4(*nvfp4.quantize(x), *nvfp4.quantize(w))
+        _check(host_f64(y), ref, dt == torch.bfloat16)
+
+
+def _w4a4_sampled(q, cfg, layer_idx, layer, m, outliers):
+    n, k = layer.n, layer.k
+    bits = synth.activations_bf16(cfg.cid, layer_idx, m, k, outliers=outliers)
+    w = synth.weights(cfg.cid, layer_idx, n, k)
+    say("w4a4 full", cfg.name, layer.name, m, n, k)
+    blob = _nvfp4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_bf16(bits))
+    y32 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.float32)
+    y16 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = sample_rows(m, 48, 7 * m + n)
+    cols = sample_rows(n, 48, 11 * n + k)
+    xf = synth.bf16_bits_as_f32(bits)
+    st_a = nvfp4.tensor_scale(xf)
+    st_w = nvfp4.tensor_scale(w)
+    ref = gemm.w4a4(*nvfp4.quantize(xf[rows], s_t=st_a), *nvfp4.quantize(w[cols], s_t=st_w))
+    _check(host_f64(y32)[np.ix_(rows, cols)], ref, False)
+    _check(host_f64(y16)[np.ix_(rows, cols)], ref, True)
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_w4a4_qwen3_prefill_full_size(li):
+    q = require_gpu()
+    cfg = configs.QWEN3_PREFILL
+    _w4a4_sampled(q, cfg, li, cfg.layers[li], 8192, cfg.outliers)
+
+
+@pytest.mark.parametrize("li,m", [(0, 4096), (1, 4096), (2, 4096), (3, 4096), (0, 32768),
+                                  (3, 16384)])
+def test_w4a4_27b_prefill_full_size(li, m):
+    q = require_gpu()
+    cfg = configs.BIG27_PREFILL
+    _w4a4_sampled(q, cfg, li, cfg.layers[li], m, cfg.outliers)
+
+
+def test_w4a4_one_hot_layout_probe():
+    """One-hot NVFP4 activations extract dequantized weight columns exactly."""
+    q = require_gpu()
+    n, k = 64, 256
+    w = synth.weights(7, 0, n, k)
+    blob = _nvfp4_blob(q, w)
+    ks = [0, 1, 15, 16, 31, 63, 100, 127, 128, 255]
+    x = np.zeros((len(ks), k), dtype=np.float32)
+    for i, kk in enumerate(ks):
+        x[i, kk] = 6.0
+    say("w4a4 one-hot probe")
+    ac, as_, at = q.quantize_nvfp4(dev_f32(x))
+    y = host_f64(q.gemm_w4a4(ac, as_, at, blob, len(ks), n, k, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    wh = nvfp4.dequantize(*nvfp4.quantize(w))
+    xh = nvfp4.dequantize(*nvfp4.quantize(x))
+    for i, kk in enumerate(ks):
+        # one exact product, then the fp32 epilogue scale (s_tA * s_tW rounded once)
+        ref = xh[i, kk] * wh[:, kk]
+        assert np.all(np.abs(y[i] - ref) <= 4 * 2.0 ** -24 * np.abs(ref)), kk
+        assert np.array_equal(y[i] == 0, ref == 0)
+
+
+def test_w4a4_deterministic_and_empty():
+    q = require_gpu()
+    m, n, k = 1024, 2048, 1024
+    bits = synth.activations_bf16(2, 9, m, k, outliers="channels")
+    w = synth.weights(2, 9, n, k)
+    say("w4a4 determinism")
+    blob = _nvfp4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_bf16(bits))
+    a = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16)
+    b = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    y0 = q.gemm_w4a4(ac, as_, at, blob, 0, n, k, y=torch.empty((0, n), device="cuda"))
+    assert y0.numel() == 0
+
+
+# --------------------------------------------------------------- W4A16 --
+
+def test_w4a16_tiny_decode():
+    q = require_gpu()
+    w = synth.weights(1, 0, 256, 512)
+    xb = synth.decode_x_bf16(1, 0, 1, 512)
+    say("w4a16 tiny")
+    blob = _int4_blob(q, w)
+    y = q.gemm_w4a16(dev_bf16(xb), blob, 256, 512, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = gemm.w4a16(xb, *int4.quantize(w))
+    _check(host_f64(y), ref, False)
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_w4a16_qwen3_decode_all_batches(li):
+    q = require_gpu()
+    cfg = configs.QWEN3_DECODE
+    layer = cfg.layers[li]
+    n, k = layer.n, layer.k
+    w = synth.weights(cfg.cid, li, n, k)
+    say("w4a16", layer.name, n, k)
+    blob = _int4_blob(q, w)
+    cols = sample_rows(n, 512, n + k)
+    rc, rs = int4.quantize(w[cols])
+    for m in cfg.ms:
+        xb = synth.decode_x_bf16(cfg.cid, li, m, k)
+        y16 = q.gemm_w4a16(dev_bf16(xb), blob, n, k, out_dtype=torch.bfloat16)
+        y32 = q.gemm_w4a16(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref = gemm.w4a16(xb, rc, rs)
+        _check(host_f64(y32)[:, cols], ref, False)
+        _check(host_f64(y16)[:, cols], ref, True)
+
+
+@pytest.mark.parametrize("m", [2, 17, 33, 50, 100])
+def test_w4a16_ragged_batches(m):
+    q = require_gpu()
+    n, k = 272, 1152
+    w = synth.weights(8, 1, n, k)
+    xb = synth.activations_bf16(8, 2, m, k)
+    say("w4a16 ragged", m)
+    blob = _int4_blob(q, w)
+    y = q.gemm_w4a16(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(host_f64(y), gemm.w4a16(xb, *int4.quantize(w)), False)
+
+
+def test_w4a16_one_hot_layout_probe():
+    q = require_gpu()
+    n, k = 48, 384
+    w = synth.weights(7, 1, n, k)
+    blob = _int4_blob(q, w)
+    ks = [0, 1, 7, 8, 31, 32, 127, 128, 200, 383]
+    x = np.zeros((len(ks), k), dtype=np.float32)
+    for i, kk in enumerate(ks):
+        x[i, kk] = 1.0
+    say("w4a16 one-hot probe")
+    y = host_f64(q.gemm_w4a16(dev_bf16(synth.to_bf16_bits(x)), blob, n, k, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    wh = int4.dequantize(*int4.quantize(w))
+    for i, kk in enumerate(ks):
+        assert np.array_equal(y[i], wh[:, kk].astype(np.float32)), kk
+
+
+# ---------------------------------------------------------------- LUT2 --
+
+@pytest.mark.parametrize("li", range(3))
+def test_lut2_gemma3_decode(li):
+    q = require_gpu()
+    cfg = configs.GEMMA3_LUT2
+    layer = cfg.layers[li]
+    n, k = layer.n, layer.k
+    w = synth.weights(cfg.cid, li, n, k)
+    say("lut2", layer.name, n, k)
+    blob = _lut2_blob(q, w)
+    cols = sample_rows(n, 96, n + k)
+    ri, rc = lut2.fit(w[cols])
+    for m in cfg.ms:
+        xb = synth.decode_x_bf16(cfg.cid, li, m, k)
+        y16 = q.gemm_lut2(dev_bf16(xb), blob, n, k, out_dtype=torch.bfloat16)
+        y32 = q.gemm_lut2(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        ref = gemm.lut2_gemm(xb, ri, rc)
+        _check(host_f64(y32)[:, cols], ref, False)
+        _check(host_f64(y16)[:, cols], ref, True)
+
+
+def test_lut2_one_hot_layout_probe_and_ragged():
+    q = require_gpu()
+    n, k = 32, 256
+    w = synth.weights(7, 2, n, k)
+    blob = _lut2_blob(q, w)
+    ks = [0, 1, 3, 4, 7, 8, 31, 32, 127, 128, 255]
+    x = np.zeros((len(ks), k), dtype=np.float32)
+    for i, kk in enumerate(ks):
+        x[i, kk] = 1.0
+    say("lut2 one-hot probe")
+    y = host_f64(q.gemm_lut2(dev_bf16(synth.to_bf16_bits(x)), blob, n, k, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    wh = lut2.dequantize(*lut2.fit(w))
+    for i, kk in enumerate(ks):
+        assert np.array_equal(y[i], wh[:, kk].astype(np.float32)), kk
+    xb = synth.activations_bf16(8, 3, 40, k)
+    y = q.gemm_lut2(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(host_f64(y), gemm.lut2_gemm(xb, *lut2.fit(w)), False)
