@@ -30,6 +30,7 @@ SOURCES = {
     "weight_prep.hip": ["-ffp-contract=off"],
     "repack.hip": [],
     "gemm_w4a4.hip": [],
+    "gemm_w4a4_coop.hip": [],
     "gemm_decode.hip": [],
 }
 

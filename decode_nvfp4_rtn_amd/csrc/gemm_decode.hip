@@ -50,25 +50,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// bf16 MFMA B operand: 8 activations x[m][k0 .. k0+8) (zero when m >= M)
-__device__ __forceinline__ bf16x8_t load_x(const uint16_t* __restrict__ x, int m, int M, int K,
-                                           int k0) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (m < M) {
-    const uint4 t = *reinterpret_cast<const uint4*>(x + int64_t(m) * K + k0);
-    v = u32x4{t.x, t.y, t.z, t.w};
-  }
-  return as_bf16x8(v);
+// A 32-bit constant held in a VGPR, so that two-constant operations such as
+// (w & mask) | bias can use one v_and_or_b32 (VOP3 on this target accepts no
+// literal constants and one scalar operand).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+  return v;
 }
 
 // INT4: dword of 8 nibbles (pairs at bits (4j, 16+4j)) -> bf16 (128+u) x 8
-__device__ __forceinline__ bf16x8_t int4_operand(uint32_t w) {
+__device__ __forceinline__ bf16x8_t int4_operand(uint32_t w, uint32_t mask, uint32_t bias) {
   u32x4 v;
-  v[0] = (w & 0x000F000Fu) | 0x43004300u;
-  v[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  v[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  v[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  v[0] = (w & mask) | bias;
+  v[1] = ((w >> 4) & mask) | bias;
+  v[2] = ((w >> 8) & mask) | bias;
+  v[3] = ((w >> 12) & mask) | bias;
   return as_bf16x8(v);
+}
+
+// LUT2: 16 2-bit indices (layout of the repacked blob) -> two bf16x8 operands
+// (sub-steps 2d and 2d+1) looked up in the row's codebook with v_perm_b32.
+__device__ __forceinline__ void lut2_operands(uint32_t w, uint32_t lo_t, uint32_t hi_t,
+                                              bf16x8_t& a0, bf16x8_t& a1) {
+  u32x4 op[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = (w >> (2 * j)) & 0x03030303u;
+    const uint32_t lo = __builtin_amdgcn_perm(0u, lo_t, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(0u, hi_t, sel);
+    op[j >> 1][2 * (j & 1)] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    op[j >> 1][2 * (j & 1) + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  }
+  a0 = as_bf16x8(op[0]);
+  a1 = as_bf16x8(op[1]);
 }
 
 template <int MT, int NTB, bool kBF16Out>
@@ -101,21 +116,64 @@ __device__ __forceinline__ void reduce_store(floatx4 (&tot)[NTB][MT], int nt0, i
   }
 }
 
-template <int MT, int NTB, bool kBF16Out>
+// Activation fragments of one 128-k group for MT m-tiles: lane l holds row
+// m0 + 16 mt + l % 16 (clamped to the last valid row: columns m >= M are
+// computed but never stored, so they need no zeroing) and k = 128 g + 32 s +
+// 8 (l / 16) + t.
+template <int MT>
+struct XFrag {
+  bf16x8_t f[4][MT];
+};
+template <int MT>
+__device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (&xr)[MT], int g) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 t = *reinterpret_cast<const uint4*>(xr[mt] + g * 128 + 32 * s);
+      X.f[s][mt] = as_bf16x8(u32x4{t.x, t.y, t.z, t.w});
+    }
+}
+
+// Each wave walks groups g0 .. g0 + gpw - 1 of NTB row tiles, one group
+// ahead in registers.  Groups past the end of k are clamped to the last one
+// and contribute zero (INT4: scale 0; LUT2: zero codebook), so the loop has no
+// branches and the compiler can count outstanding loads exactly.
+// Each wave owns groups g0 .. g0 + gpw - 1 of NTB row tiles.  Weight loads
+// (HBM) for a whole chunk of WMAX groups are issued at once, so the wave's
+// entire k-range is in flight; activation fragments (small, L2-resident) are
+// fetched one group ahead.  Groups past the wave's range or past k are
+// clamped to a valid address and contribute zero (scale 0), so the loop has
+// no branches and the compiler can count outstanding loads exactly.
+template <int MT, int NTB, int WMAX, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
                                                         const uint8_t* __restrict__ blob,
                                                         int64_t codes_off, int64_t sc_off, int M,
                                                         int m0, int N, int K,
                                                         void* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
   const int gpw = (G + KW - 1) / KW;
-  const int g0 = wave * gpw, g1 = min(G, g0 + gpw);
+  const int g0 = wave * gpw;
   const int nt0 = blockIdx.x * NTB;
   const int NT16 = N / 16;
-  const uint4* codes = reinterpret_cast<const uint4*>(blob + codes_off);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(blob + sc_off);
-  const bf16x8_t ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const uint32_t one2 = vconst(0x3F803F80u);
+  const bf16x8_t ones = as_bf16x8(u32x4{one2, one2, one2, one2});
+  const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
+
+  const uint16_t* xr[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    xr[mt] = x + int64_t(min(m0 + mt * 16 + (lane & 15), M - 1)) * K + 8 * (lane >> 4);
+  const uint4* wp[NTB];
+  const uint2* sp[NTB];
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt) {
+    const int64_t tile = min(nt0 + nt, NT16 - 1);
+    wp[nt] = reinterpret_cast<const uint4*>(blob + codes_off) + tile * G * 64 + lane;
+    sp[nt] = reinterpret_cast<const uint2*>(blob + sc_off + (tile * G * 16 + 4 * (lane >> 4)) * 2);
+  }
 
   floatx4 tot[NTB][MT];
 #pragma unroll
@@ -123,73 +181,90 @@ __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restri
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = g0; g < g1; ++g) {
-    uint4 wv[NTB];
-    uint2 sv[NTB];
+  for (int c0 = 0; c0 < gpw; c0 += WMAX) {
+    uint4 wv[WMAX][NTB];
+    uint2 sv[WMAX][NTB];
 #pragma unroll
-    for (int nt = 0; nt < NTB; ++nt) {
-      const int tile = min(nt0 + nt, NT16 - 1);
-      wv[nt] = load_nt16(&codes[(int64_t(tile) * G + g) * 64 + lane]);
-      sv[nt] = *reinterpret_cast<const uint2*>(scales + (int64_t(tile) * G + g) * 16 +
-                                               4 * (lane >> 4));
-    }
-    bf16x8_t xf[4][MT];
-    floatx4 xs[MT];
+    for (int i = 0; i < WMAX; ++i) {
+      const int gc = min(g0 + min(c0 + i, gpw - 1), G - 1);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      xs[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        xf[s][mt] = load_x(x, m0 + mt * 16 + (lane & 15), M, K, g * 128 + 32 * s + 8 * (lane >> 4));
-        xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, xf[s][mt], xs[mt], 0, 0, 0);
+      for (int nt = 0; nt < NTB; ++nt) {
+        wv[i][nt] = load_nt16(wp[nt] + gc * 64);
+        sv[i][nt] = sp[nt][gc * 4];
       }
     }
+    XFrag<MT> xf;
+    load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
 #pragma unroll
-    for (int nt = 0; nt < NTB; ++nt) {
-      floatx4 acc[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const uint32_t wd[4] = {wv[nt].x, wv[nt].y, wv[nt].z, wv[nt].w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8_t a = int4_operand(wd[s]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf[s][mt], acc[mt], 0, 0, 0);
-      }
-      const float sc[4] = {__uint_as_float(sv[nt].x << 16), __uint_as_float(sv[nt].x & 0xFFFF0000u),
-                           __uint_as_float(sv[nt].y << 16), __uint_as_float(sv[nt].y & 0xFFFF0000u)};
+    for (int i = 0; i < WMAX; ++i) {
+      const int g = g0 + c0 + i;
+      XFrag<MT> xn;
+      if (i + 1 < WMAX) load_xfrag<MT>(xn, xr, min(g + 1, G - 1));   // compile-time condition
+      floatx4 xs[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const float off = 136.0f * xs[mt][0];
+        xs[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tot[nt][mt][i] += sc[i] * (acc[mt][i] - off);
+        for (int s = 0; s < 4; ++s)
+          xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, xf.f[s][mt], xs[mt], 0, 0, 0);
       }
+      const float live = (c0 + i < gpw && g < G) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        floatx4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t wd[4] = {wv[i][nt].x, wv[i][nt].y, wv[i][nt].z, wv[i][nt].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t a = int4_operand(wd[s], nib_mask, bf16_128);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf.f[s][mt], acc[mt], 0, 0, 0);
+        }
+        const uint2 sb = sv[i][nt];
+        const float sc[4] = {live * __uint_as_float(sb.x << 16),
+                             live * __uint_as_float(sb.x & 0xFFFF0000u),
+                             live * __uint_as_float(sb.y << 16),
+                             live * __uint_as_float(sb.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const float off = 136.0f * xs[mt][0];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tot[nt][mt][r] += sc[r] * (acc[mt][r] - off);
+        }
+      }
+      if (i + 1 < WMAX) xf = xn;
     }
   }
   reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
-template <int MT, int NTB, bool kBF16Out>
+template <int MT, int NTB, int WMAX, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ blob,
                                                        int64_t codes_off, int64_t book_off, int M,
                                                        int m0, int N, int K,
                                                        void* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
   const int gpw = (G + KW - 1) / KW;
-  const int g0 = wave * gpw, g1 = min(G, g0 + gpw);
+  const int g0 = wave * gpw;
   const int nt0 = blockIdx.x * NTB;
   const int NT16 = N / 16;
-  const uint2* codes = reinterpret_cast<const uint2*>(blob + codes_off);
-  const uint2* book = reinterpret_cast<const uint2*>(blob + book_off);
 
+  const uint16_t* xr[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    xr[mt] = x + int64_t(min(m0 + mt * 16 + (lane & 15), M - 1)) * K + 8 * (lane >> 4);
+  const uint2* wp[NTB];
   uint32_t lo_t[NTB], hi_t[NTB];
 #pragma unroll
   for (int nt = 0; nt < NTB; ++nt) {
-    const int tile = min(nt0 + nt, NT16 - 1);
-    const uint2 b = book[tile * 16 + (lane & 15)];
+    const int64_t tile = min(nt0 + nt, NT16 - 1);
+    wp[nt] = reinterpret_cast<const uint2*>(blob + codes_off) + tile * G * 64 + lane;
+    const uint2 b = reinterpret_cast<const uint2*>(blob + book_off)[tile * 16 + (lane & 15)];
     lo_t[nt] = b.x;
     hi_t[nt] = b.y;
   }
@@ -200,68 +275,101 @@ __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restric
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = g0; g < g1; ++g) {
-    uint2 wv[NTB];
+  for (int c0 = 0; c0 < gpw; c0 += WMAX) {
+    uint2 wv[WMAX][NTB];
 #pragma unroll
-    for (int nt = 0; nt < NTB; ++nt) {
-      const int tile = min(nt0 + nt, NT16 - 1);
-      wv[nt] = load_nt8(&codes[(int64_t(tile) * G + g) * 64 + lane]);
+    for (int i = 0; i < WMAX; ++i) {
+      const int gc = min(g0 + min(c0 + i, gpw - 1), G - 1);
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) wv[i][nt] = load_nt8(wp[nt] + gc * 64);
     }
-    bf16x8_t xf[4][MT];
+    XFrag<MT> xf;
+    load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int i = 0; i < WMAX; ++i) {
+      const int g = g0 + c0 + i;
+      XFrag<MT> xn;
+      if (i + 1 < WMAX) load_xfrag<MT>(xn, xr, min(g + 1, G - 1));   // compile-time condition
+      const uint32_t keep = (c0 + i < gpw && g < G) ? 0xFFFFFFFFu : 0u;  // else zero codebook
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        xf[s][mt] = load_x(x, m0 + mt * 16 + (lane & 15), M, K, g * 128 + 32 * s + 8 * (lane >> 4));
+      for (int nt = 0; nt < NTB; ++nt) {
+        const uint32_t lo = lo_t[nt] & keep, hi = hi_t[nt] & keep;
+        bf16x8_t a[4];
+        lut2_operands(wv[i][nt].x, lo, hi, a[0], a[1]);
+        lut2_operands(wv[i][nt].y, lo, hi, a[2], a[3]);
 #pragma unroll
-    for (int nt = 0; nt < NTB; ++nt) {
-      const uint32_t wd[2] = {wv[nt].x, wv[nt].y};
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        u32x4 op[2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t sel = (wd[d] >> (2 * j)) & 0x03030303u;
-          const uint32_t lo = __builtin_amdgcn_perm(0u, lo_t[nt], sel);
-          const uint32_t hi = __builtin_amdgcn_perm(0u, hi_t[nt], sel);
-          op[j >> 1][2 * (j & 1)] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-          op[j >> 1][2 * (j & 1) + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-        }
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          const bf16x8_t a = as_bf16x8(op[sl]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            tot[nt][mt] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf[2 * d + sl][mt], tot[nt][mt], 0, 0, 0);
-        }
+          for (int s = 0; s < 4; ++s)
+            tot[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], xf.f[s][mt], tot[nt][mt],
+                                                                  0, 0, 0);
       }
+      if (i + 1 < WMAX) xf = xn;
     }
   }
   reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
-template <bool kLut, int MT, int NTB>
+template <bool kLut, int MT, int NTB, int WMAX>
 hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L, int M, int m0,
                          int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int blocks = (N / 16 + NTB - 1) / NTB;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (kLut) {
+  if constexpr (kLut) {
     if (y_dtype == 1)
-      lut2_kernel<MT, NTB, true><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M,
-                                                            m0, N, K, y);
+      lut2_kernel<MT, NTB, WMAX, true><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+                                                                  L.aux_off, M, m0, N, K, y);
     else
-      lut2_kernel<MT, NTB, false><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M,
-                                                             m0, N, K, y);
+      lut2_kernel<MT, NTB, WMAX, false><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+                                                                   L.aux_off, M, m0, N, K, y);
   } else {
     if (y_dtype == 1)
-      w4a16_kernel<MT, NTB, true><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M,
-                                                             m0, N, K, y);
+      w4a16_kernel<MT, NTB, WMAX, true><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+                                                                   L.aux_off, M, m0, N, K, y);
     else
-      w4a16_kernel<MT, NTB, false><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off,
-                                                              M, m0, N, K, y);
+      w4a16_kernel<MT, NTB, WMAX, false><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+                                                                    L.aux_off, M, m0, N, K, y);
   }
   return hipGetLastError();
+}
+
+// Largest chunk whose weight registers fit without spilling (the INT4 operand
+// is 16 bytes per lane and group per row tile, the LUT2 one 8).
+constexpr int chunk_cap(bool lut, int mt, int ntb) {
+  return lut ? 16 : (mt * ntb == 1 ? 16 : (mt * ntb == 2 ? 8 : 4));
+}
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+
+// Chunk of groups whose weight loads a wave issues at once.  Loads in flight
+// hide HBM latency; a chunk boundary costs roughly one extra round trip and a
+// padded slot one wasted load, so pick the size that minimises the sum.
+int pick_chunk(int gpw, int cap) {
+  static const int kSizes[] = {2, 4, 6, 8, 12, 16};
+  int best = 2, best_cost = 1 << 30;
+  for (int w : kSizes) {
+    if (w > cap) break;
+    const int chunks = (gpw + w - 1) / w;
+    const int cost = chunks * w + 2 * chunks;
+    if (cost < best_cost) best = w, best_cost = cost;
+  }
+  return best;
+}
+
+template <bool kLut, int MT, int NTB>
+hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout& L, int M,
+                           int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
+  constexpr int kCap = chunk_cap(kLut, MT, NTB);
+  switch (pick_chunk((K / 128 + KW - 1) / KW, kCap)) {
+    // pick_chunk never exceeds kCap; the min() only keeps unused cases from
+    // instantiating kernels that would spill
+    case 2: return launch_decode<kLut, MT, NTB, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 4: return launch_decode<kLut, MT, NTB, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 6: return launch_decode<kLut, MT, NTB, cmin(6, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 8: return launch_decode<kLut, MT, NTB, cmin(8, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 12: return launch_decode<kLut, MT, NTB, cmin(12, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    default: return launch_decode<kLut, MT, NTB, cmin(16, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+  }
 }
 
 template <bool kLut>
@@ -269,13 +377,18 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
                              void* y, int y_dtype, hipStream_t s) {
   const BlobLayout L = blob_layout(kLut ? 2 : 1, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
+  // two row tiles per block when there are enough tiles to keep every CU busy
+  // (N >= 6144 gives at least 192 blocks of 512 threads)
+  const bool wide = n / 16 >= 384;
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = static_cast<int>(m - m0 < 32 ? m - m0 : 32);
     hipError_t e;
     if (rows <= 16)
-      e = launch_decode<kLut, 1, 1>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s);
+      e = wide ? launch_decode_w<kLut, 1, 2>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s)
+               : launch_decode_w<kLut, 1, 1>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s);
     else
-      e = launch_decode<kLut, 2, 1>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s);
+      e = wide ? launch_decode_w<kLut, 2, 2>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s)
+               : launch_decode_w<kLut, 2, 1>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -21,6 +21,11 @@
 // Products of dequantized operands are exact in fp32; only the accumulation
 // rounds.  The ceiling of this exact formulation is the dense fp16 MFMA rate.
 //
+// Two kernels share this arithmetic.  Problems with at least 256 tiles of
+// 256 x 256 go to the block-cooperative kernel (gemm_w4a4_coop.hip), which
+// dequantizes each code once per block into fp16 LDS tiles.  Smaller problems
+// use the per-wave kernel below, whose 4x smaller tiles keep every CU busy.
+//
 // Tiling.  Block tile 128 (n) x 128 (m), k-step 128, four waves in 2 x 2,
 // each wave 64 x 64 = 4 x 4 MFMA tiles.  Codes and scales of both operands are
 // staged through LDS (double buffered, one barrier per k-step) in their
@@ -45,17 +50,9 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128;
 constexpr int RS = 80;             // LDS row stride in bytes (64 data + 16 pad)
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // 4 waves, 2 (n) x 2 (m)
 constexpr int GROUP_M = 8;
-
-struct __attribute__((aligned(16))) Smem {
-  uint8_t wc[2][BN * RS];
-  uint8_t xc[2][BM * RS];
-  uint8_t ws[2][BN * 8];
-  uint8_t xs[2][BM * 8];
-};
 
 __device__ __forceinline__ half2_t h2(uint32_t w, int sel) {
   switch (sel) {
@@ -84,12 +81,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <bool kBF16Out>
-__global__ __launch_bounds__(kThreads, 2) void w4a4_kernel(
+__device__ __forceinline__ uint32_t dword(const uint4& v, int d) {
+  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// WN x WM MFMA tiles (16 x 16 each) per wave; block tile BN x BM with 2 x 2 waves.
+template <int WN, int WM, bool kBF16Out>
+__global__ __launch_bounds__(kThreads) void w4a4_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
     int64_t ws_off, int M, int N, int K, void* __restrict__ y) {
-  __shared__ Smem sm;
+  constexpr int BN = 32 * WN, BM = 32 * WM;
+  constexpr int WU = BN * 4 / kThreads;   // 16-byte W code units per thread per stage
+  constexpr int XU = BM * 4 / kThreads;   // 16-byte X code units per thread per stage
+  constexpr int SU = (BN + BM + kThreads - 1) / kThreads;  // 8-byte scale rows per thread
+  __shared__ __attribute__((aligned(16))) uint8_t wc_s[2][BN * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t xc_s[2][BM * RS];
+  __shared__ __attribute__((aligned(16))) uint8_t sc_s[2][(BN + BM) * 8];
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
@@ -110,50 +119,64 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_kernel(
   const uint8_t* wcodes = blob + wc_off;
   const uint8_t* wscales = blob + ws_off;
 
-  floatx4 acc[4][4];
+  floatx4 acc[WN][WM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WN; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pw[2], px[2];
-  uint2 ps;
+  uint4 pw[WU], px[XU];
+  uint2 ps[SU];
   auto gload = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WU; ++i) {
       const int u = i * kThreads + tid;
-      const int nt = tn * 8 + (u >> 6);
+      const int nt = tn * (BN / 16) + (u >> 6);
       pw[i] = nt < NT16 ? *reinterpret_cast<const uint4*>(
                               wcodes + (int64_t(nt) * KT + ks) * 1024 + (u & 63) * 16)
                         : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = i * kThreads + tid;
       const int m = m0 + (u >> 2);
       px[i] = m < M ? *reinterpret_cast<const uint4*>(xcodes + int64_t(m) * (K / 2) + ks * 64 +
                                                       (u & 3) * 16)
                     : make_uint4(0, 0, 0, 0);
     }
-    if (tid < 128) {
-      const int nt = tn * 8 + (tid >> 4);
-      ps = nt < NT16 ? *reinterpret_cast<const uint2*>(
-                           wscales + (int64_t(nt) * KT + ks) * 128 + (tid & 15) * 8)
-                     : make_uint2(0, 0);
-    } else {
-      const int m = m0 + tid - 128;
-      ps = m < M ? *reinterpret_cast<const uint2*>(xscales + int64_t(m) * (K / 16) + ks * 8)
-                 : make_uint2(0, 0);
+#pragma unroll
+    for (int i = 0; i < SU; ++i) {
+      const int r = i * kThreads + tid;   // 0 .. BN+BM-1; W rows first
+      if (r >= BN + BM) {
+        ps[i] = make_uint2(0, 0);
+      } else if (r < BN) {
+        const int nt = tn * (BN / 16) + (r >> 4);
+        ps[i] = nt < NT16 ? *reinterpret_cast<const uint2*>(
+                                wscales + (int64_t(nt) * KT + ks) * 128 + (r & 15) * 8)
+                          : make_uint2(0, 0);
+      } else {
+        const int m = m0 + r - BN;
+        ps[i] = m < M ? *reinterpret_cast<const uint2*>(xscales + int64_t(m) * (K / 16) + ks * 8)
+                      : make_uint2(0, 0);
+      }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WU; ++i) {
       const int u = i * kThreads + tid;
       const int wr = (u >> 6) * 16 + ((u & 63) >> 2);
-      *reinterpret_cast<uint4*>(&sm.wc[buf][wr * RS + (u & 3) * 16]) = pw[i];
-      *reinterpret_cast<uint4*>(&sm.xc[buf][(u >> 2) * RS + (u & 3) * 16]) = px[i];
+      *reinterpret_cast<uint4*>(&wc_s[buf][wr * RS + (u & 3) * 16]) = pw[i];
     }
-    if (tid < 128)
-      *reinterpret_cast<uint2*>(&sm.ws[buf][tid * 8]) = ps;
-    else
-      *reinterpret_cast<uint2*>(&sm.xs[buf][(tid - 128) * 8]) = ps;
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = i * kThreads + tid;
+      *reinterpret_cast<uint4*>(&xc_s[buf][(u >> 2) * RS + (u & 3) * 16]) = px[i];
+    }
+#pragma unroll
+    for (int i = 0; i < SU; ++i)
+      if (i * kThreads + tid < BN + BM)
+        *reinterpret_cast<uint2*>(&sc_s[buf][(i * kThreads + tid) * 8]) = ps[i];
   };
 
   gload(0);
@@ -165,38 +188,32 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_kernel(
     const int buf = ks & 1;
     if (ks + 1 < KT) gload(ks + 1);
 
-    uint4 wraw[4], xraw[4];
-    uint32_t wsc[4], xsc[4];
+    uint4 wraw[WN], xraw[WM];
+    uint32_t wsc[WN], xsc[WM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wn * 64 + i * 16 + r;
-      wraw[i] = *reinterpret_cast<const uint4*>(&sm.wc[buf][row * RS + q * 16]);
-      wsc[i] = *reinterpret_cast<const uint16_t*>(&sm.ws[buf][row * 8 + 2 * q]);
+    for (int i = 0; i < WN; ++i) {
+      const int row = wn * (BN / 2) + i * 16 + r;
+      wraw[i] = *reinterpret_cast<const uint4*>(&wc_s[buf][row * RS + q * 16]);
+      wsc[i] = *reinterpret_cast<const uint16_t*>(&sc_s[buf][row * 8 + 2 * q]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wm * 64 + j * 16 + r;
-      xraw[j] = *reinterpret_cast<const uint4*>(&sm.xc[buf][row * RS + q * 16]);
-      xsc[j] = *reinterpret_cast<const uint16_t*>(&sm.xs[buf][row * 8 + 2 * q]);
+    for (int j = 0; j < WM; ++j) {
+      const int row = wm * (BM / 2) + j * 16 + r;
+      xraw[j] = *reinterpret_cast<const uint4*>(&xc_s[buf][row * RS + q * 16]);
+      xsc[j] = *reinterpret_cast<const uint16_t*>(&sc_s[buf][(BN + row) * 8 + 2 * q]);
     }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {          // d = 2c + s
-      half8_t wf[4], xf[4];
+    for (int d = 0; d < 4; ++d) {          // d = 2c + s: group 2q + c, half s
+      half8_t xf[WM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = d == 0 ? wraw[i].x : d == 1 ? wraw[i].y : d == 2 ? wraw[i].z : wraw[i].w;
-        wf[i] = dequant8(w, scale2(wsc[i], d >> 1));
+      for (int j = 0; j < WM; ++j) xf[j] = dequant8(dword(xraw[j], d), scale2(xsc[j], d >> 1));
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const half8_t wf = dequant8(dword(wraw[i], d), scale2(wsc[i], d >> 1));
+#pragma unroll
+        for (int j = 0; j < WM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = d == 0 ? xraw[j].x : d == 1 ? xraw[j].y : d == 2 ? xraw[j].z : xraw[j].w;
-        xf[j] = dequant8(w, scale2(xsc[j], d >> 1));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[i], xf[j], acc[i][j], 0, 0, 0);
     }
 
     if (ks + 1 < KT) sstore(buf ^ 1);
@@ -206,12 +223,12 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_kernel(
   // epilogue: scale by s_tA * s_tW and store 4 consecutive n per lane
   const float st = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + wn * 64 + i * 16 + 4 * q;
+  for (int i = 0; i < WN; ++i) {
+    const int n = n0 + wn * (BN / 2) + i * 16 + 4 * q;
     if (n >= N) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + wm * 64 + j * 16 + r;
+    for (int j = 0; j < WM; ++j) {
+      const int m = m0 + wm * (BM / 2) + j * 16 + r;
       if (m >= M) continue;
       const floatx4 v = acc[i][j] * st;
       if (kBF16Out) {
@@ -226,21 +243,37 @@ __global__ __launch_bounds__(kThreads, 2) void w4a4_kernel(
   }
 }
 
+template <int WN, int WM>
+hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                       const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
+                       int64_t k, void* y, int y_dtype, hipStream_t s) {
+  constexpr int BN = 32 * WN, BM = 32 * WM;
+  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+  if (y_dtype == 1)
+    w4a4_kernel<WN, WM, true><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob,
+                                                          L.codes_off, L.aux_off, int(m), int(n),
+                                                          int(k), y);
+  else
+    w4a4_kernel<WN, WM, false><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob,
+                                                           L.codes_off, L.aux_off, int(m), int(n),
+                                                           int(k), y);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                             const void* w_packed, int64_t m, int64_t n, int64_t k, void* y,
                             int y_dtype, hipStream_t s) {
   const BlobLayout L = blob_layout(0, n, k);
-  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
-  if (y_dtype == 1)
-    w4a4_kernel<true><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob, L.codes_off,
-                                                 L.aux_off, int(m), int(n), int(k), y);
-  else
-    w4a4_kernel<false><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob, L.codes_off,
-                                                  L.aux_off, int(m), int(n), int(k), y);
-  return hipGetLastError();
+  // The block-cooperative 256x256 kernel holds one block per CU (its LDS
+  // double buffer is 160 KiB), so it needs at least one tile per CU; smaller
+  // problems take the 128x128 per-wave kernel, which spreads 4x more blocks.
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (big_tiles >= 256)
+    return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype, s);
+  return launch_tile<4, 4>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
 }
 
 }  // namespace qlin

@@ -1,0 +1,291 @@
+// NVFP4 W4A4 prefill GEMM for gfx950, block-cooperative dequantization.
+//
+//   Y[m,n] = s_tA s_tW sum_g sA[m,g] sW[n,g] sum_{k in g} E2M1(a[m,k]) E2M1(w[n,k])
+//
+// Same exact arithmetic as the register-dequant kernel (fp16 operands that
+// hold E2M1 * E4M3 exactly, v_mfma_f32_16x16x32_f16, fp32 accumulation, the
+// tensor scales in the epilogue), organised so that every code is dequantized
+// once per 256 x 256 block instead of once per wavefront that uses it.  On
+// gfx950 VALU work and MFMA work share the SIMD issue slots (measured:
+// non-interleaved they simply add up), so dequantization per MFMA is the
+// quantity to minimise: 1 VALU op per MFMA here against 4 in the
+// register-dequant design.
+//
+// Block 256 (n) x 256 (m), 8 wavefronts in 2 (n) x 4 (m), each 128 x 64
+// (8 x 4 MFMA tiles, 128 fp32 accumulators per lane; 2 waves per SIMD).  K
+// advances 64 per stage.  Per stage every thread owns one of the 512 rows (256
+// weight rows, then 256 activation rows):
+//   global -> registers: 32 code bytes + 4 E4M3 scale bytes,
+//   registers -> fp16: 64 values (cvt fp4->f16, exact pk_mul by the scale),
+//   registers -> LDS: 8 x 16 bytes.
+// The fp16 tiles are double buffered in LDS (2 stages x 2 operands x 256 rows
+// x 160 bytes = 160 KiB, one block per CU); stage s+1 is dequantized while
+// the MFMAs of stage s run, one 16-byte dequant store after every MFMA row.
+// Codes for stage s+2 are loaded at the start of stage s (two register sets).
+// LDS rows are padded from 128 to 160 bytes, which measured fewest bank
+// conflicts for the 16-byte fragment reads and the row-wise stores together.
+// Tiles are visited XCD-major (consecutive workgroups go to different XCDs,
+// so each XCD gets a contiguous run of tiles) and in groups of 8 m-tiles, so
+// the tiles in flight on one XCD share weight and activation panels in L2.
+#include "qlin_internal.hpp"
+
+namespace qlin {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = 256, BM = 256, BK = 64;
+constexpr int GROUP_M = 8;
+
+__device__ __forceinline__ half2_t cvt2(uint32_t w, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  }
+}
+
+// 8 codes -> 8 exact fp16 products with the group scale, packed for one store
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, half2_t s) {
+  return u32x4{__builtin_bit_cast(uint32_t, cvt2(w, 0) * s),
+               __builtin_bit_cast(uint32_t, cvt2(w, 1) * s),
+               __builtin_bit_cast(uint32_t, cvt2(w, 2) * s),
+               __builtin_bit_cast(uint32_t, cvt2(w, 3) * s)};
+}
+
+__device__ __forceinline__ half2_t scale_h2(uint32_t w4, int g) {
+  float f;
+  switch (g) {
+    case 0: f = __builtin_amdgcn_cvt_f32_fp8(w4, 0); break;
+    case 1: f = __builtin_amdgcn_cvt_f32_fp8(w4, 1); break;
+    case 2: f = __builtin_amdgcn_cvt_f32_fp8(w4, 2); break;
+    default: f = __builtin_amdgcn_cvt_f32_fp8(w4, 3); break;
+  }
+  const _Float16 h = static_cast<_Float16>(f);
+  return half2_t{h, h};
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4& v, int d) {
+  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// WAVES = 4: 2 x 2 waves of 128 x 128 (1 wave per SIMD);
+// WAVES = 8: 2 (n) x 4 (m) waves of 128 x 64 (2 waves per SIMD).
+template <int WAVES, int RS, bool kBF16Out>
+__global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
+    const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
+    const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
+    int64_t ws_off, int M, int N, int K, void* __restrict__ y) {
+  constexpr int NTHR = WAVES * 64;
+  constexpr int TILE_BYTES = 256 * RS;
+  constexpr int WGM = WAVES / 2;          // waves along m
+  constexpr int TN = 8;                   // 16-row MFMA tiles per wave along n (128)
+  constexpr int TM = BM / WGM / 16;       // along m: 8 (128) or 4 (64)
+  constexpr int ROWS = 512 / NTHR;        // rows each thread dequantizes per stage (2 or 1)
+  constexpr int DW = 8 * ROWS;            // dwords of codes per thread per stage
+  constexpr int STEP = 2 * TN / DW;       // fragment iterations per dequantized dword
+  static_assert(STEP >= 1 && (2 * TN) % DW == 0, "dequant interleave");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [2][W tile, X tile]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int total = tiles_m * tiles_n;
+
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (t / in_group) * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (t % in_group) % gsz;
+  const int tn = (t % in_group) / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int KT = K / 128;
+  const int S = K / BK;
+  const int NT16 = N / 16;
+
+  // dequantization rows of this thread: row j of 512 = tid + j * NTHR; rows < 256
+  // are weight rows n0 + row, the rest activation rows m0 + row - 256
+  const uint8_t* src[ROWS];
+  const uint8_t* ssrc[ROWS];
+  bool ok[ROWS], isw[ROWS];
+  int lrow[ROWS];
+#pragma unroll
+  for (int j = 0; j < ROWS; ++j) {
+    const int row = tid + j * NTHR;
+    isw[j] = row < 256;
+    lrow[j] = row & 255;
+    if (isw[j]) {
+      const int wrow = n0 + row;
+      ok[j] = (wrow >> 4) < NT16;
+      src[j] = blob + wc_off + (int64_t(wrow >> 4) * KT * 16 + (wrow & 15)) * 64;
+      ssrc[j] = blob + ws_off + (int64_t(wrow >> 4) * KT * 16 + (wrow & 15)) * 8;
+    } else {
+      const int xrow = m0 + row - 256;
+      ok[j] = xrow < M;
+      src[j] = xcodes + int64_t(xrow) * (K / 2);
+      ssrc[j] = xscales + int64_t(xrow) * (K / 16);
+    }
+  }
+
+  // codes + scales of one stage for this thread's rows; two sets (ping-pong) so
+  // the loads for stage st+2 are issued at the start of stage st
+  struct Regs {
+    uint4 c[ROWS][2];
+    uint32_t sc[ROWS];
+  };
+  Regs ra, rb;
+  auto gload = [&](Regs& R, int st) {
+#pragma unroll
+    for (int j = 0; j < ROWS; ++j) {
+      int64_t coff, soff;
+      if (isw[j]) {
+        coff = int64_t(st >> 1) * 16 * 64 + (st & 1) * 32;
+        soff = int64_t(st >> 1) * 16 * 8 + (st & 1) * 4;
+      } else {
+        coff = int64_t(st) * 32;
+        soff = int64_t(st) * 4;
+      }
+      if (ok[j]) {
+        const uint4* p = reinterpret_cast<const uint4*>(src[j] + coff);
+        R.c[j][0] = p[0];
+        R.c[j][1] = p[1];
+        R.sc[j] = *reinterpret_cast<const uint32_t*>(ssrc[j] + soff);
+      } else {
+        R.c[j][0] = R.c[j][1] = make_uint4(0, 0, 0, 0);
+        R.sc[j] = 0;
+      }
+    }
+  };
+  // dequantize dword e (0 .. DW-1) of this thread's rows into LDS buffer buf
+  auto dq_store = [&](const Regs& R, int buf, int e) {
+    const int j = e >> 3, d = e & 7;
+    const u32x4 h = dequant8(pick(R.c[j][d >> 2], d & 3), scale_h2(R.sc[j], d >> 1));
+    uint8_t* dst = smem + buf * 2 * TILE_BYTES + (isw[j] ? 0 : TILE_BYTES) + lrow[j] * RS + d * 16;
+    *reinterpret_cast<u32x4*>(dst) = h;
+  };
+
+  floatx4 acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  gload(ra, 0);
+#pragma unroll
+  for (int e = 0; e < DW; ++e) dq_store(ra, 0, e);
+  gload(rb, 1);   // S >= 2 (K % 128 == 0)
+  __syncthreads();
+
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r = lane & 15, q = lane >> 4;
+  const int wbase = (wn * 128 + r) * RS + q * 16;
+  const int xbase = (wm * (TM * 16) + r) * RS + q * 16;
+
+  // one stage: MFMAs on LDS buffer `buf` while `nxt` (stage st+1's codes) is
+  // dequantized into the other buffer
+  auto stage = [&](int buf, const Regs& nxt) {
+    const uint8_t* wt = smem + buf * 2 * TILE_BYTES;
+    const uint8_t* xt = wt + TILE_BYTES;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      half8_t xf[TM];
+#pragma unroll
+      for (int j = 0; j < TM; ++j)
+        xf[j] = *reinterpret_cast<const half8_t*>(xt + xbase + j * 16 * RS + s * 64);
+      half8_t wf = *reinterpret_cast<const half8_t*>(wt + wbase + s * 64);
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        half8_t wn_f = wf;
+        if (i + 1 < TN)
+          wn_f = *reinterpret_cast<const half8_t*>(wt + wbase + (i + 1) * 16 * RS + s * 64);
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf[j], acc[i][j], 0, 0, 0);
+        // on the last stage this writes the idle buffer, which nothing reads again
+        const int it = s * TN + i;
+        if (it % STEP == 0) dq_store(nxt, buf ^ 1, it / STEP);
+        wf = wn_f;
+      }
+    }
+  };
+  // The prefetches are unconditional (the stage index is clamped; reloading the
+  // last stage is harmless): a load under a branch makes the compiler wait for
+  // every outstanding load at the join, which would expose the full latency.
+  for (int st = 0; st < S; st += 2) {
+    // even stage: buffer 0; rb holds stage st+1; ra is free -> stage st+2
+    gload(ra, min(st + 2, S - 1));
+    stage(0, rb);
+    __syncthreads();
+    // odd stage: buffer 1; ra holds stage st+2; rb is free -> stage st+3
+    gload(rb, min(st + 3, S - 1));
+    stage(1, ra);
+    __syncthreads();
+  }
+
+  const float stv = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+#pragma unroll
+  for (int i = 0; i < TN; ++i) {
+    const int n = n0 + wn * 128 + i * 16 + 4 * q;
+    if (n >= N) continue;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      const int m = m0 + wm * (TM * 16) + j * 16 + r;
+      if (m >= M) continue;
+      const floatx4 v = acc[i][j] * stv;
+      if (kBF16Out) {
+        uint2 o;
+        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+      }
+    }
+  }
+}
+
+template <int WAVES, int RS>
+hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                       const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
+                       int64_t k, void* y, int y_dtype, hipStream_t s) {
+  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+  const size_t lds = 2 * 2 * 256 * RS;
+  // the dynamic-LDS limit is a per-function attribute: set it once
+  static const hipError_t attr = [lds] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_coop_kernel<WAVES, RS, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_coop_kernel<WAVES, RS, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    return e;
+  }();
+  if (attr != hipSuccess) return attr;
+  if (y_dtype == 1)
+    w4a4_coop_kernel<WAVES, RS, true><<<tiles, WAVES * 64, lds, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y);
+  else
+    w4a4_coop_kernel<WAVES, RS, false><<<tiles, WAVES * 64, lds, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a4_coop(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const float* a_ts, const void* w_packed, int64_t m, int64_t n,
+                                 int64_t k, void* y, int y_dtype, hipStream_t s) {
+  const BlobLayout L = blob_layout(0, n, k);
+  const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
+  return launch_coop<8, 160>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
+}
+
+}  // namespace qlin

@@ -90,6 +90,9 @@ hipError_t launch_repack(int fmt, int64_t n, int64_t k, const uint8_t* codes,
 hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
                             const float* a_ts, const void* w_packed, int64_t m, int64_t n,
                             int64_t k, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_w4a4_coop(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const float* a_ts, const void* w_packed, int64_t m, int64_t n,
+                                 int64_t k, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n,
                              int64_t k, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm_lut2(const void* x, const void* w_packed, int64_t m, int64_t n,

@@ -259,3 +259,37 @@ def test_lut2_one_hot_layout_probe_and_ragged():
     y = q.gemm_lut2(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
     torch.cuda.synchronize()
     _check(host_f64(y), gemm.lut2_gemm(xb, *lut2.fit(w)), False)
+
+
+# ---------------------------------------------- decode k-chunking sweep --
+# The decode kernels split k over 8 wavefronts and load each wavefront's
+# groups in chunks (2 .. 16 groups) chosen from the group count; these shapes
+# reach every chunk size, ragged group counts (idle and partly idle
+# wavefronts), both row-tile widths (N >= 6144 uses two 16-row tiles per
+# block) and both batch tilings (<= 16 and 17 .. 32 rows, and > 32 rows).
+
+_CHUNK_K = [640, 2176, 5248, 8192, 8320, 15360, 20608]
+_CHUNK_CASES = [(272, k) for k in _CHUNK_K] + [(6160, k) for k in _CHUNK_K if k <= 8320]
+
+
+@pytest.mark.parametrize("fmt", ["int4", "lut2"])
+@pytest.mark.parametrize("n,k", _CHUNK_CASES)
+def test_decode_k_chunking(fmt, n, k):
+    q = require_gpu()
+    w = synth.weights(9, k, n, k)
+    say("decode chunking", fmt, n, k)
+    cols = sample_rows(n, 64, n * 3 + k)
+    if fmt == "int4":
+        blob = _int4_blob(q, w)
+        ref_w = int4.quantize(w[cols])
+        fn, ref_fn = q.gemm_w4a16, gemm.w4a16
+    else:
+        blob = _lut2_blob(q, w)
+        ref_w = lut2.fit(w[cols])
+        fn, ref_fn = q.gemm_lut2, gemm.lut2_gemm
+    del w
+    for m in (3, 20, 40):
+        xb = synth.activations_bf16(9, m, m, k)
+        y = fn(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(host_f64(y)[:, cols], ref_fn(xb, *ref_w), False)
