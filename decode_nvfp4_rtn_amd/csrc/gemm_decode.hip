@@ -135,16 +135,15 @@ __device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (
     }
 }
 
-// Each wave walks groups g0 .. g0 + gpw - 1 of NTB row tiles, one group
-// ahead in registers.  Groups past the end of k are clamped to the last one
-// and contribute zero (INT4: scale 0; LUT2: zero codebook), so the loop has no
-// branches and the compiler can count outstanding loads exactly.
-// Each wave owns groups g0 .. g0 + gpw - 1 of NTB row tiles.  Weight loads
-// (HBM) for a whole chunk of WMAX groups are issued at once, so the wave's
-// entire k-range is in flight; activation fragments (small, L2-resident) are
-// fetched one group ahead.  Groups past the wave's range or past k are
-// clamped to a valid address and contribute zero (scale 0), so the loop has
-// no branches and the compiler can count outstanding loads exactly.
+// Each wave owns groups g0 .. g0 + gpw - 1 of NTB row tiles and walks them in
+// chunks of WMAX groups.  A chunk's weight loads (HBM) are issued at once;
+// activation fragments (small, L2-resident) follow one group ahead.  The
+// arithmetic of a chunk runs in two phases so that no VALU instruction waits
+// on an MFMA it has just issued: first every group's MFMA chains (independent,
+// so they stream through the matrix core back to back), then every group's
+// fp32 scale multiply-add.  Slots past the wave's range or past k are clamped
+// to a valid address and contribute zero (their scales are replaced by 0),
+// so the loop has no branches and the compiler can count outstanding loads.
 template <int MT, int NTB, int WMAX, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
                                                         const uint8_t* __restrict__ blob,
@@ -158,8 +157,10 @@ __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restri
   const int g0 = wave * gpw;
   const int nt0 = blockIdx.x * NTB;
   const int NT16 = N / 16;
-  const uint32_t one2 = vconst(0x3F803F80u);
-  const bf16x8_t ones = as_bf16x8(u32x4{one2, one2, one2, one2});
+  // -136 in every bf16 lane: an MFMA chain against it yields -136 * sum x, the
+  // start value that turns sum x (128 + u) into sum x q (u = q + 8)
+  const uint32_t m136 = vconst(0xC308C308u);
+  const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
 
   const uint16_t* xr[MT];
@@ -193,48 +194,53 @@ __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restri
         sv[i][nt] = sp[nt][gc * 4];
       }
     }
+    // phase 1: MFMA chains of every group of the chunk
+    floatx4 acc[WMAX][NTB][MT];
     XFrag<MT> xf;
     load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
-      const int g = g0 + c0 + i;
       XFrag<MT> xn;
-      if (i + 1 < WMAX) load_xfrag<MT>(xn, xr, min(g + 1, G - 1));   // compile-time condition
+      if (i + 1 < WMAX) load_xfrag<MT>(xn, xr, min(g0 + c0 + i + 1, G - 1));   // compile-time
       floatx4 xs[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         xs[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, xf.f[s][mt], xs[mt], 0, 0, 0);
+          xs[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, xf.f[s][mt], xs[mt], 0, 0, 0);
       }
-      const float live = (c0 + i < gpw && g < G) ? 1.0f : 0.0f;
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) {
-        floatx4 acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc[i][nt][mt] = xs[mt];
         const uint32_t wd[4] = {wv[i][nt].x, wv[i][nt].y, wv[i][nt].z, wv[i][nt].w};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const bf16x8_t a = int4_operand(wd[s], nib_mask, bf16_128);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf.f[s][mt], acc[mt], 0, 0, 0);
-        }
-        const uint2 sb = sv[i][nt];
-        const float sc[4] = {live * __uint_as_float(sb.x << 16),
-                             live * __uint_as_float(sb.x & 0xFFFF0000u),
-                             live * __uint_as_float(sb.y << 16),
-                             live * __uint_as_float(sb.y & 0xFFFF0000u)};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const float off = 136.0f * xs[mt][0];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tot[nt][mt][r] += sc[r] * (acc[mt][r] - off);
+            acc[i][nt][mt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf.f[s][mt], acc[i][nt][mt], 0, 0, 0);
         }
       }
       if (i + 1 < WMAX) xf = xn;
+    }
+    // phase 2: tot += group scale * (sum x q), in fp32, per group
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      const bool live = c0 + i < gpw && g0 + c0 + i < G;
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        const uint32_t s01 = live ? sv[i][nt].x : 0u, s23 = live ? sv[i][nt].y : 0u;
+        const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
+                             __uint_as_float(s23 << 16), __uint_as_float(s23 & 0xFFFF0000u)};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            tot[nt][mt][r] = fmaf(sc[r], acc[i][nt][mt][r], tot[nt][mt][r]);
+      }
     }
   }
   reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
@@ -269,11 +275,15 @@ __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restric
     hi_t[nt] = b.y;
   }
 
-  floatx4 tot[NTB][MT];
+  // two accumulator sets, even and odd groups, so consecutive MFMAs of a tile
+  // do not wait on each other's results
+  floatx4 tot2[2][NTB][MT];
 #pragma unroll
-  for (int nt = 0; nt < NTB; ++nt)
+  for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) tot2[e][nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     uint2 wv[WMAX][NTB];
@@ -301,12 +311,17 @@ __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restric
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            tot[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], xf.f[s][mt], tot[nt][mt],
-                                                                  0, 0, 0);
+            tot2[i & 1][nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a[s], xf.f[s][mt], tot2[i & 1][nt][mt], 0, 0, 0);
       }
       if (i + 1 < WMAX) xf = xn;
     }
   }
+  floatx4 tot[NTB][MT];
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = tot2[0][nt][mt] + tot2[1][nt][mt];
   reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
@@ -336,7 +351,7 @@ hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L
 // Largest chunk whose weight registers fit without spilling (the INT4 operand
 // is 16 bytes per lane and group per row tile, the LUT2 one 8).
 constexpr int chunk_cap(bool lut, int mt, int ntb) {
-  return lut ? 16 : (mt * ntb == 1 ? 16 : (mt * ntb == 2 ? 8 : 4));
+  return lut ? 16 : (mt * ntb == 1 ? 16 : (mt * ntb == 2 ? 8 : 2));
 }
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -364,7 +379,7 @@ hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout&
     // pick_chunk never exceeds kCap; the min() only keeps unused cases from
     // instantiating kernels that would spill
     case 2: return launch_decode<kLut, MT, NTB, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-    case 4: return launch_decode<kLut, MT, NTB, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 4: return launch_decode<kLut, MT, NTB, cmin(4, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
     case 6: return launch_decode<kLut, MT, NTB, cmin(6, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
     case 8: return launch_decode<kLut, MT, NTB, cmin(8, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
     case 12: return launch_decode<kLut, MT, NTB, cmin(12, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
