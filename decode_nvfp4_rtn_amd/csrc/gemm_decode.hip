@@ -325,6 +325,156 @@ __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restric
   reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
+// Persistent variant for one m-tile (M <= 16) and K <= 128 * KW * GW.  Wave w
+// owns groups [GW w, GW w + GW) of every row tile, so its activation
+// fragments -- and, for INT4, the -136 * sum x seeds -- are the same for all
+// tiles: they are loaded and computed once per wave and stay in registers.
+// One or two blocks per CU walk the row tiles t = blockIdx.x, + gridDim.x, ...
+// with the next tile's weights (two register sets) in flight while the
+// current one is dequantized, multiplied and reduced; no activation load sits
+// between them in the load queue, so the arithmetic waits only for its own
+// tile.  Used when every block gets at least two tiles.
+template <int GW, bool kLut>
+struct PersistTile;
+template <int GW>
+struct PersistTile<GW, false> {
+  uint4 w[GW];
+  uint2 s[GW];
+};
+template <int GW>
+struct PersistTile<GW, true> {
+  uint2 w[GW];
+  uint2 book;
+};
+
+// Blocks of this kernel that fit on one CU: two when the registers allow four
+// waves per SIMD (LUT2, or INT4 with two groups per wave), else one.
+constexpr int persist_blocks_per_cu(int gw, bool lut) { return (lut || gw == 2) ? 2 : 1; }
+
+template <int GW, bool kLut, bool kBF16Out>
+__global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void decode_persist_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob, int64_t codes_off,
+    int64_t aux_off, int M, int N, int K, void* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int G = K / 128;
+  const int g0 = wave * GW;
+  const int T = N / 16;
+  const uint32_t m136 = vconst(0xC308C308u);
+  const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
+  const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
+
+  const uint16_t* xr = x + int64_t(min(lane & 15, M - 1)) * K + 8 * (lane >> 4);
+  bf16x8_t xf[GW][4];
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    const int gc = min(g0 + i, G - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
+      xf[i][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+    }
+  }
+  floatx4 xs[GW];
+  if constexpr (!kLut) {
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      xs[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, xf[i][s], xs[i], 0, 0, 0);
+    }
+  }
+
+  auto load = [&](PersistTile<GW, kLut>& A, int t) {
+#pragma unroll
+    for (int i = 0; i < GW; ++i) {
+      const int64_t gi = int64_t(t) * G + min(g0 + i, G - 1);
+      if constexpr (kLut) {
+        A.w[i] = load_nt8(reinterpret_cast<const uint2*>(blob + codes_off) + gi * 64 + lane);
+      } else {
+        A.w[i] = load_nt16(reinterpret_cast<const uint4*>(blob + codes_off) + gi * 64 + lane);
+        A.s[i] = reinterpret_cast<const uint2*>(blob + aux_off)[gi * 4 + (lane >> 4)];
+      }
+    }
+    if constexpr (kLut)
+      A.book = reinterpret_cast<const uint2*>(blob + aux_off)[int64_t(t) * 16 + (lane & 15)];
+  };
+
+  // per tile: each wave's partial sums go to one of two LDS slots (alternating
+  // by tile, so one barrier per tile suffices); wave 0 adds them and stores
+  __shared__ floatx4 red[2][KW][64];
+  auto finish = [&](const PersistTile<GW, kLut>& A, int t, int slot) {
+    floatx4 tot;
+    if constexpr (kLut) {
+      floatx4 t2[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const uint32_t keep = g0 + i < G ? 0xFFFFFFFFu : 0u;   // else zero codebook
+        const uint32_t lo = A.book.x & keep, hi = A.book.y & keep;
+        bf16x8_t a[4];
+        lut2_operands(A.w[i].x, lo, hi, a[0], a[1]);
+        lut2_operands(A.w[i].y, lo, hi, a[2], a[3]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          t2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], xf[i][s], t2[i & 1], 0, 0, 0);
+      }
+      tot = t2[0] + t2[1];
+    } else {
+      floatx4 acc[GW];
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        acc[i] = xs[i];
+        const uint32_t wd[4] = {A.w[i].x, A.w[i].y, A.w[i].z, A.w[i].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4_operand(wd[s], nib_mask, bf16_128),
+                                                           xf[i][s], acc[i], 0, 0, 0);
+      }
+      tot = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const bool live = g0 + i < G;
+        const uint32_t s01 = live ? A.s[i].x : 0u, s23 = live ? A.s[i].y : 0u;
+        const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
+                             __uint_as_float(s23 << 16), __uint_as_float(s23 & 0xFFFF0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[r] = fmaf(sc[r], acc[i][r], tot[r]);
+      }
+    }
+    red[slot][wave][lane] = tot;
+    __syncthreads();
+    if (wave == 0) {
+      floatx4 v = red[slot][0][lane];
+#pragma unroll
+      for (int w = 1; w < KW; ++w) v += red[slot][w][lane];
+      const int n = t * 16 + 4 * (lane >> 4), m = lane & 15;
+      if (m < M) {
+        if (kBF16Out) {
+          uint2 o;
+          o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+          o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
+        } else {
+          *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+        }
+      }
+    }
+  };
+
+  // the launch guarantees gridDim.x <= T, so every block has a first tile
+  const int stride = gridDim.x;
+  PersistTile<GW, kLut> A, B;
+  int t = blockIdx.x;
+  load(A, t);
+  for (; t < T; t += 2 * stride) {
+    load(B, min(t + stride, T - 1));
+    finish(A, t, 0);
+    load(A, min(t + 2 * stride, T - 1));
+    if (t + stride < T) finish(B, t + stride, 1);   // block-uniform condition
+  }
+}
+
 template <bool kLut, int MT, int NTB, int WMAX>
 hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L, int M, int m0,
                          int N, int K, void* y, int y_dtype, hipStream_t s) {
@@ -387,6 +537,19 @@ hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout&
   }
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 template <bool kLut>
 hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int64_t n, int64_t k,
                              void* y, int y_dtype, hipStream_t s) {
@@ -395,6 +558,24 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
   // two row tiles per block when there are enough tiles to keep every CU busy
   // (N >= 6144 gives at least 192 blocks of 512 threads)
   const bool wide = n / 16 >= 384;
+  // one m-tile, K <= 4096 and at least two row tiles per CU: persistent kernel
+  const int G = static_cast<int>(k / 128);
+  const int cus = device_cu_count();
+  if (m <= 16 && G <= KW * 4 && cus > 0 && n / 16 >= 2 * cus) {
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const int M = int(m), N = int(n), K = int(k), T = int(n / 16);
+    auto run = [&](auto kern, int per_cu) {
+      // every block must own at least two tiles, and the grid never exceeds T
+      const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
+      kern<<<grid, KW * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M, N, K, y);
+      return hipGetLastError();
+    };
+    if (G <= KW * 2)
+      return y_dtype == 1 ? run(decode_persist_kernel<2, kLut, true>, persist_blocks_per_cu(2, kLut))
+                          : run(decode_persist_kernel<2, kLut, false>, persist_blocks_per_cu(2, kLut));
+    return y_dtype == 1 ? run(decode_persist_kernel<4, kLut, true>, persist_blocks_per_cu(4, kLut))
+                        : run(decode_persist_kernel<4, kLut, false>, persist_blocks_per_cu(4, kLut));
+  }
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = static_cast<int>(m - m0 < 32 ? m - m0 : 32);
     hipError_t e;
