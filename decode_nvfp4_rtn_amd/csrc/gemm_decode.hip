@@ -86,21 +86,21 @@ __device__ __forceinline__ void lut2_operands(uint32_t w, uint32_t lo_t, uint32_
   a1 = as_bf16x8(op[1]);
 }
 
-template <int MT, int NTB, bool kBF16Out>
+template <int MT, int NTB, int KWT, bool kBF16Out>
 __device__ __forceinline__ void reduce_store(floatx4 (&tot)[NTB][MT], int nt0, int m0, int M,
                                              int N, void* __restrict__ y) {
-  __shared__ floatx4 red[KW][NTB][MT][64];
+  __shared__ floatx4 red[KWT][NTB][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int nt = 0; nt < NTB; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) red[wave][nt][mt][lane] = tot[nt][mt];
   __syncthreads();
-  for (int t = threadIdx.x; t < NTB * MT * 64; t += KW * 64) {
+  for (int t = threadIdx.x; t < NTB * MT * 64; t += KWT * 64) {
     const int nt = t / (MT * 64), mt = (t / 64) % MT, ln = t % 64;
     floatx4 s = red[0][nt][mt][ln];
 #pragma unroll
-    for (int w = 1; w < KW; ++w) s += red[w][nt][mt][ln];
+    for (int w = 1; w < KWT; ++w) s += red[w][nt][mt][ln];
     const int n = (nt0 + nt) * 16 + 4 * (ln >> 4);
     const int m = m0 + mt * 16 + (ln & 15);
     if (m < M && n < N) {
@@ -144,8 +144,8 @@ __device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (
 // fp32 scale multiply-add.  Slots past the wave's range or past k are clamped
 // to a valid address and contribute zero (their scales are replaced by 0),
 // so the loop has no branches and the compiler can count outstanding loads.
-template <int MT, int NTB, int WMAX, bool kBF16Out>
-__global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
+template <int MT, int NTB, int WMAX, int KWT, bool kBF16Out>
+__global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
                                                         const uint8_t* __restrict__ blob,
                                                         int64_t codes_off, int64_t sc_off, int M,
                                                         int m0, int N, int K,
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restri
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
-  const int gpw = (G + KW - 1) / KW;
+  const int gpw = (G + KWT - 1) / KWT;
   const int g0 = wave * gpw;
   const int nt0 = blockIdx.x * NTB;
   const int NT16 = N / 16;
@@ -243,11 +243,11 @@ __global__ __launch_bounds__(KW * 64) void w4a16_kernel(const uint16_t* __restri
       }
     }
   }
-  reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
+  reduce_store<MT, NTB, KWT, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
-template <int MT, int NTB, int WMAX, bool kBF16Out>
-__global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restrict__ x,
+template <int MT, int NTB, int WMAX, int KWT, bool kBF16Out>
+__global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ blob,
                                                        int64_t codes_off, int64_t book_off, int M,
                                                        int m0, int N, int K,
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restric
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
-  const int gpw = (G + KW - 1) / KW;
+  const int gpw = (G + KWT - 1) / KWT;
   const int g0 = wave * gpw;
   const int nt0 = blockIdx.x * NTB;
   const int NT16 = N / 16;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(KW * 64) void lut2_kernel(const uint16_t* __restric
   for (int nt = 0; nt < NTB; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = tot2[0][nt][mt] + tot2[1][nt][mt];
-  reduce_store<MT, NTB, kBF16Out>(tot, nt0, m0, M, N, y);
+  reduce_store<MT, NTB, KWT, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
 // Persistent variant for one m-tile (M <= 16) and K <= 128 * KW * GW.  Wave w
@@ -475,24 +475,24 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
   }
 }
 
-template <bool kLut, int MT, int NTB, int WMAX>
+template <bool kLut, int MT, int NTB, int WMAX, int KWT>
 hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L, int M, int m0,
                          int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int blocks = (N / 16 + NTB - 1) / NTB;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   if constexpr (kLut) {
     if (y_dtype == 1)
-      lut2_kernel<MT, NTB, WMAX, true><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+      lut2_kernel<MT, NTB, WMAX, KWT, true><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
                                                                   L.aux_off, M, m0, N, K, y);
     else
-      lut2_kernel<MT, NTB, WMAX, false><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+      lut2_kernel<MT, NTB, WMAX, KWT, false><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
                                                                    L.aux_off, M, m0, N, K, y);
   } else {
     if (y_dtype == 1)
-      w4a16_kernel<MT, NTB, WMAX, true><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+      w4a16_kernel<MT, NTB, WMAX, KWT, true><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
                                                                    L.aux_off, M, m0, N, K, y);
     else
-      w4a16_kernel<MT, NTB, WMAX, false><<<blocks, KW * 64, 0, s>>>(xp, blob, L.codes_off,
+      w4a16_kernel<MT, NTB, WMAX, KWT, false><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
                                                                     L.aux_off, M, m0, N, K, y);
   }
   return hipGetLastError();
@@ -500,8 +500,11 @@ hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L
 
 // Largest chunk whose weight registers fit without spilling (the INT4 operand
 // is 16 bytes per lane and group per row tile, the LUT2 one 8).
-constexpr int chunk_cap(bool lut, int mt, int ntb) {
-  return lut ? 16 : (mt * ntb == 1 ? 16 : (mt * ntb == 2 ? 8 : 2));
+// Largest chunk whose registers fit without spilling (8 waves per block may
+// use up to 256 VGPRs; 16 waves per block, up to 128).
+constexpr int chunk_cap(bool lut, int mt, int ntb, int kwt) {
+  return kwt == 16 ? (lut ? 8 : (mt * ntb == 1 ? 6 : 2))
+                   : (lut ? 16 : (mt * ntb == 1 ? 16 : (mt * ntb == 2 ? 8 : 2)));
 }
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -521,19 +524,19 @@ int pick_chunk(int gpw, int cap) {
   return best;
 }
 
-template <bool kLut, int MT, int NTB>
+template <bool kLut, int MT, int NTB, int KWT>
 hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout& L, int M,
                            int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
-  constexpr int kCap = chunk_cap(kLut, MT, NTB);
-  switch (pick_chunk((K / 128 + KW - 1) / KW, kCap)) {
+  constexpr int kCap = chunk_cap(kLut, MT, NTB, KWT);
+  switch (pick_chunk((K / 128 + KWT - 1) / KWT, kCap)) {
     // pick_chunk never exceeds kCap; the min() only keeps unused cases from
     // instantiating kernels that would spill
-    case 2: return launch_decode<kLut, MT, NTB, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-    case 4: return launch_decode<kLut, MT, NTB, cmin(4, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-    case 6: return launch_decode<kLut, MT, NTB, cmin(6, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-    case 8: return launch_decode<kLut, MT, NTB, cmin(8, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-    case 12: return launch_decode<kLut, MT, NTB, cmin(12, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-    default: return launch_decode<kLut, MT, NTB, cmin(16, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 2: return launch_decode<kLut, MT, NTB, 2, KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 4: return launch_decode<kLut, MT, NTB, cmin(4, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 6: return launch_decode<kLut, MT, NTB, cmin(6, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 8: return launch_decode<kLut, MT, NTB, cmin(8, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 12: return launch_decode<kLut, MT, NTB, cmin(12, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    default: return launch_decode<kLut, MT, NTB, cmin(16, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
   }
 }
 
@@ -578,13 +581,14 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
   }
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = static_cast<int>(m - m0 < 32 ? m - m0 : 32);
+    const int a = int(m), b = int(m0), c = int(n), d = int(k);
     hipError_t e;
     if (rows <= 16)
-      e = wide ? launch_decode_w<kLut, 1, 2>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s)
-               : launch_decode_w<kLut, 1, 1>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s);
+      e = wide ? launch_decode_w<kLut, 1, 2, KW>(x, blob, L, a, b, c, d, y, y_dtype, s)
+               : launch_decode_w<kLut, 1, 1, KW>(x, blob, L, a, b, c, d, y, y_dtype, s);
     else
-      e = wide ? launch_decode_w<kLut, 2, 2>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s)
-               : launch_decode_w<kLut, 2, 1>(x, blob, L, int(m), int(m0), int(n), int(k), y, y_dtype, s);
+      e = wide ? launch_decode_w<kLut, 2, 2, KW>(x, blob, L, a, b, c, d, y, y_dtype, s)
+               : launch_decode_w<kLut, 2, 1, KW>(x, blob, L, a, b, c, d, y, y_dtype, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
