@@ -72,6 +72,7 @@ def main():
                     help="rows of X per layer in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-sweep", action="store_true")
+    ap.add_argument("--no-bf16-reference", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 device copies of 256 MiB (a kernel of known traffic, "
                          "to scale the FETCH_SIZE/WRITE_SIZE counters of a --pmc run)")
@@ -268,6 +269,65 @@ def main():
                 out[f"m{m}"] = round(float(np.mean([v["gbps"] for v in vals])), 1)
         return out
 
+    # ------------------------------------------- BF16 reference points ----
+    # The pages state their speed-ups against BF16; torch's bf16 matmul
+    # (hipBLASLt) on the same shapes is that reference here: prefill
+    # Y = X W^T at M=8192 (TFLOP/s) and decode GEMV at M=1 and 16 (GB/s,
+    # weights rotated over > 600 MB like the decode sweep).
+    bf16_ref = {}
+    if not args.no_bf16_reference:
+        for p in P:
+            L = p["L"]
+            wb = torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev) * (L.k ** -0.5)
+            ref_ms = []
+            for _ in range(3):
+                torch.matmul(p["x"], wb.t())
+            torch.cuda.synchronize()
+            for _ in range(10):
+                a, b = E(enable_timing=True), E(enable_timing=True)
+                a.record()
+                torch.matmul(p["x"], wb.t())
+                b.record()
+                b.synchronize()
+                ref_ms.append(a.elapsed_time(b))
+            med = float(np.median(ref_ms))
+            bf16_ref[f"prefill/{L.name}"] = {
+                "us": round(med * 1e3, 1),
+                "tflops": round(2.0 * M * L.n * L.k / med / 1e9, 1)}
+            del wb
+        for d in D:
+            L = d["L"]
+            copies = [torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev)
+                      for _ in range(int(np.ceil(600e6 / (2.0 * L.n * L.k))))]
+            for m in (1, 16):
+                xb = d["x"][m]
+                yb = torch.empty((m, L.n), dtype=torch.bfloat16, device=dev)
+                for c in copies[:2]:
+                    torch.matmul(xb, c.t(), out=yb)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for c in copies:
+                        torch.matmul(xb, c.t(), out=yb)
+                g.replay()
+                torch.cuda.synchronize()
+                t = []
+                for _ in range(5):
+                    a, b = E(enable_timing=True), E(enable_timing=True)
+                    a.record()
+                    g.replay()
+                    b.record()
+                    b.synchronize()
+                    t.append(a.elapsed_time(b) / len(copies))
+                del g
+                med = float(np.median(t))
+                by = 2.0 * L.n * L.k + 2.0 * m * L.k + 2.0 * m * L.n
+                bf16_ref[f"decode/{L.name}/m{m}"] = {"us": round(med * 1e3, 2),
+                                                    "gbps": round(by / med / 1e6, 1)}
+            del copies
+            torch.cuda.empty_cache()
+        _progress("bf16 reference points measured")
+
     # --------------------------------------------------- CPU baseline ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -323,6 +383,10 @@ def main():
             "w4a16_gbps_mean_over_layers": _agg("w4a16", dec.ms),
             "lut2_gbps_mean_over_layers": _agg("lut2", lut.ms),
             "decode_sweep": sweep,
+            "bf16_reference": bf16_ref,
+            "w4a4_gemm_speedup_vs_bf16": (
+                round(sum(v["us"] for k, v in bf16_ref.items() if k.startswith("prefill/"))
+                      / (gemm_ms_step * 1e3), 3) if bf16_ref else None),
             "decode_timing": "events around the replay of a HIP graph of back-to-back launches "
                              "rotating over >600 MB of weight copies (Infinity Cache defeated)",
         },

@@ -63,9 +63,7 @@ template <bool kBF16>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x, int64_t nvec,
                                                         uint32_t* __restrict__ partial) {
   uint32_t m = 0;
-  const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
-    uint4 v = load_nt16(&x[i]);
+  auto fold = [&](const uint4& v) {
     if (kBF16) {
       m = abs_bits_bf16_pair(v.x, m);
       m = abs_bits_bf16_pair(v.y, m);
@@ -79,24 +77,33 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
       a = a > c ? a : c;
       m = m > a ? m : a;
     }
+  };
+  const int64_t stride = int64_t(gridDim.x) * kThreads;
+  int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  // four independent 16-byte loads in flight per thread, then the remainder
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const uint4 v0 = load_nt16(&x[i]), v1 = load_nt16(&x[i + stride]);
+    const uint4 v2 = load_nt16(&x[i + 2 * stride]), v3 = load_nt16(&x[i + 3 * stride]);
+    fold(v0);
+    fold(v1);
+    fold(v2);
+    fold(v3);
   }
+  for (; i < nvec; i += stride) fold(load_nt16(&x[i]));
   m = block_max_u32(m);
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
 // E4M3 (OCP E4M3FN) encoding of a non-negative binary32 value: round to
-// nearest, ties to even, saturating at 448 (0x7E).
+// nearest, ties to even, saturating at 448 (0x7E).  The hardware converter
+// rounds to nearest-even but does not saturate (it returns NaN above 464), so
+// the value is clamped to 448 first; a NaN input also becomes 448 (fminf
+// returns the other operand).  An exhaustive sweep of every non-negative
+// binary32 pattern on gfx950 found this identical to the integer encoder
+// (mantissa rounding, exponent rebias, subnormal quantum 2^-9, saturation).
 __device__ __forceinline__ uint32_t enc_e4m3(float q) {
-  if (!(q < 448.0f)) return 0x7Eu;
-  if (q < 0.015625f) {                      // below 2^-6: subnormal quantum 2^-9
-    return static_cast<uint32_t>(__builtin_rintf(q * 512.0f));  // 0..8 (8 == 2^-6)
-  }
-  uint32_t u = __float_as_uint(q);
-  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);  // round mantissa to 3 bits, RNE
-  r &= 0xFFF00000u;
-  uint32_t e = (r >> 23) - 120u;                // biased E4M3 exponent (1..15)
-  uint32_t code = (e << 3) | ((r >> 20) & 7u);
-  return code > 0x7Eu ? 0x7Eu : code;
+  const float c = __builtin_fminf(q, 448.0f);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0u, false) & 0xFFu;
 }
 
 // Exact binary32 value of a non-negative E4M3 code (0..0x7E).
@@ -106,13 +113,21 @@ __device__ __forceinline__ float dec_e4m3(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// E2M1 code of a binary32 value: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the
-// even code, saturating at 6; the sign bit is copied.
-__device__ __forceinline__ uint32_t enc_e2m1(float y) {
-  float a = __builtin_fabsf(y);
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-               (a >= 3.5f) + (a > 5.0f);
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+// Eight E2M1 codes of the binary32 values y[0..7] (element 2i in the low
+// nibble of byte i): nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
+// saturating at 6, sign copied (also for results that round to zero).
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts two values per
+// instruction into one byte of the destination; an exhaustive sweep of every
+// non-NaN binary32 pattern on gfx950 found it identical to the comparison
+// chain  code = (a>.25)+(a>=.75)+(a>1.25)+(a>=1.75)+(a>2.5)+(a>=3.5)+(a>5),
+// a = |y|, with the sign bit of y.
+__device__ __forceinline__ uint32_t enc_e2m1_x8(const float* y) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
 }
 
 template <bool kBF16>
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-    uint32_t sc = (d == 0.0f) ? 0u : enc_e4m3(a / d);
+    const uint32_t sc = (d == 0.0f) ? 0u : enc_e4m3(a / d);
     const float p = dec_e4m3(sc) * s_t;
     uint32_t w0 = 0, w1 = 0;
     if (p == 0.0f) {
@@ -175,11 +190,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
       }
     } else {
       const float inv = 1.0f / p;
+      float y[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w0 |= enc_e2m1(v[i] * inv) << (4 * i);
-        w1 |= enc_e2m1(v[8 + i] * inv) << (4 * i);
-      }
+      for (int i = 0; i < 16; ++i) y[i] = v[i] * inv;
+      w0 = enc_e2m1_x8(y);
+      w1 = enc_e2m1_x8(y + 8);
     }
     reinterpret_cast<uint2*>(codes)[g] = make_uint2(w0, w1);
     scales[g] = static_cast<uint8_t>(sc);
