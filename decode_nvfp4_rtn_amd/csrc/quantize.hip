@@ -11,9 +11,10 @@
 //   a non-negative float, which orders like an unsigned integer).
 // Pass 2 (encode): every block first folds the partial maxima (a few KiB,
 //   L2-resident) into amax and s_t -- so no third launch and no atomics are
-//   needed and the result is deterministic -- then each thread encodes whole
-//   16-element groups: one 32 B (bf16) or 64 B (fp32) load, one 8 B code
-//   store and one scale byte per group.  Both passes are HBM-bound streams.
+//   needed and the result is deterministic -- then each lane encodes one
+//   16-byte vector (half a bf16 group, a quarter of an fp32 group), the lanes
+//   of a group sharing their maxima by shuffles.  Both passes are HBM-bound
+//   streams with every wavefront access one contiguous run.
 //
 // This translation unit is compiled without fast-math and with
 // -ffp-contract=off: every division is the correctly rounded binary32
@@ -113,53 +114,26 @@ __device__ __forceinline__ float dec_e4m3(uint32_t c) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// Eight E2M1 codes of the binary32 values y[0..7] (element 2i in the low
-// nibble of byte i): nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
-// saturating at 6, sign copied (also for results that round to zero).
-// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts two values per
-// instruction into one byte of the destination; an exhaustive sweep of every
-// non-NaN binary32 pattern on gfx950 found it identical to the comparison
-// chain  code = (a>.25)+(a>=.75)+(a>1.25)+(a>=1.75)+(a>2.5)+(a>=3.5)+(a>5),
-// a = |y|, with the sign bit of y.
-__device__ __forceinline__ uint32_t enc_e2m1_x8(const float* y) {
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
-  return w;
-}
+// E2M1 encoding uses v_cvt_scalef32_pk_fp4_f32 with scale 1.0: two binary32
+// values per instruction (the first into the low nibble) into one byte of
+// the destination: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the even code,
+// saturating at 6, sign copied also for results that round to zero.  An
+// exhaustive sweep of every non-NaN binary32 pattern on gfx950 found it
+// identical to the comparison chain  code = (a>.25)+(a>=.75)+(a>1.25)+
+// (a>=1.75)+(a>2.5)+(a>=3.5)+(a>5), a = |y|, with the sign bit of y.
 
-template <bool kBF16>
-__device__ __forceinline__ void load_group(const void* x, int64_t g, float v[16]) {
-  if (kBF16) {
-    const uint4* p = reinterpret_cast<const uint4*>(x) + 2 * g;
-    uint4 a = load_nt16(p), b = load_nt16(p + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(x) + 4 * g;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 t = load_nt16(p + i);
-      v[4 * i] = __uint_as_float(t.x);
-      v[4 * i + 1] = __uint_as_float(t.y);
-      v[4 * i + 2] = __uint_as_float(t.z);
-      v[4 * i + 3] = __uint_as_float(t.w);
-    }
-  }
-}
-
-// Pass 2: tensor scale, then group scales and element codes.
+// Pass 2: tensor scale, then group scales and element codes.  Each lane
+// loads one contiguous 16-byte vector (8 bf16 or 4 fp32 values), so a
+// wavefront load is one contiguous 1 KiB run; the LPG lanes of a group
+// (2 for bf16, 4 for fp32) exchange their partial maxima with lane shuffles,
+// each computes the same group scale, and each encodes its own values.
 template <bool kBF16>
 __global__ __launch_bounds__(kThreads) void encode_kernel(
-    const void* __restrict__ x, int64_t ngroups, uint8_t* __restrict__ codes,
+    const uint4* __restrict__ x, int64_t nvec, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale, int static_scale,
     const uint32_t* __restrict__ partial, int npartial) {
+  constexpr int LPG = kBF16 ? 2 : 4;   // lanes per 16-element group
+  constexpr int EPL = 16 / LPG;        // elements per lane
   float s_t;
   if (static_scale) {
     s_t = *tensor_scale;
@@ -172,32 +146,53 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
   }
   const float d = 6.0f * s_t;
 
+  // the stride and the vector count are multiples of LPG and every group
+  // starts at a multiple of LPG, so the lanes of a group are active together
   const int64_t stride = int64_t(gridDim.x) * kThreads;
-  for (int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x; g < ngroups; g += stride) {
-    float v[16];
-    load_group<kBF16>(x, g, v);
-    float a = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const uint4 t = load_nt16(&x[i]);
+    float v[EPL];
+    if (kBF16) {
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-    const uint32_t sc = (d == 0.0f) ? 0u : enc_e4m3(a / d);
-    const float p = dec_e4m3(sc) * s_t;
-    uint32_t w0 = 0, w1 = 0;
-    if (p == 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        w0 |= ((__float_as_uint(v[i]) >> 31) << 3) << (4 * i);
-        w1 |= ((__float_as_uint(v[8 + i]) >> 31) << 3) << (4 * i);
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
       }
     } else {
-      const float inv = 1.0f / p;
-      float y[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) y[i] = v[i] * inv;
-      w0 = enc_e2m1_x8(y);
-      w1 = enc_e2m1_x8(y + 8);
+      v[0] = __uint_as_float(t.x);
+      v[1] = __uint_as_float(t.y);
+      v[2] = __uint_as_float(t.z);
+      v[3] = __uint_as_float(t.w);
     }
-    reinterpret_cast<uint2*>(codes)[g] = make_uint2(w0, w1);
-    scales[g] = static_cast<uint8_t>(sc);
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) a = __builtin_fmaxf(a, __builtin_fabsf(v[j]));
+#pragma unroll
+    for (int o = 1; o < LPG; o <<= 1) a = __builtin_fmaxf(a, __shfl_xor(a, o, 64));
+    const uint32_t sc = (d == 0.0f) ? 0u : enc_e4m3(a / d);
+    const float p = dec_e4m3(sc) * s_t;
+    uint32_t w = 0;
+    if (p == 0.0f) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) w |= ((__float_as_uint(v[j]) >> 31) << 3) << (4 * j);
+    } else {
+      const float inv = 1.0f / p;
+      float y[EPL];
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) y[j] = v[j] * inv;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+      if (kBF16) {
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4 % EPL], y[5 % EPL], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6 % EPL], y[7 % EPL], 1.0f, 3);
+      }
+    }
+    if (kBF16)
+      reinterpret_cast<uint32_t*>(codes)[i] = w;          // 8 codes of this lane
+    else
+      reinterpret_cast<uint16_t*>(codes)[i] = static_cast<uint16_t>(w);   // 4 codes
+    if ((i & (LPG - 1)) == 0) scales[i / LPG] = static_cast<uint8_t>(sc);
   }
 }
 
@@ -226,15 +221,17 @@ hipError_t launch_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t ngroups = total / 16;
-  int64_t blocks = (ngroups + kThreads - 1) / kThreads;
+  const int64_t nvec = bf16 ? total / 8 : total / 4;   // 16-byte vectors
+  int64_t blocks = (nvec + kThreads - 1) / kThreads;
   if (blocks > kMaxEncodeBlocks) blocks = kMaxEncodeBlocks;
   if (bf16)
     encode_kernel<true><<<static_cast<int>(blocks), kThreads, 0, s>>>(
-        x, ngroups, codes, scales, tensor_scale, static_scale, partial, npart);
+        static_cast<const uint4*>(x), nvec, codes, scales, tensor_scale, static_scale, partial,
+        npart);
   else
     encode_kernel<false><<<static_cast<int>(blocks), kThreads, 0, s>>>(
-        x, ngroups, codes, scales, tensor_scale, static_scale, partial, npart);
+        static_cast<const uint4*>(x), nvec, codes, scales, tensor_scale, static_scale, partial,
+        npart);
   return hipGetLastError();
 }
 
