@@ -113,10 +113,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   const int NT16 = N / 16;
 
   // dequantization rows of this thread: row j of 512 = tid + j * NTHR; rows < 256
-  // are weight rows n0 + row, the rest activation rows m0 + row - 256
+  // are weight rows n0 + row, the rest activation rows m0 + row - 256.  Rows
+  // past N or M are clamped to the last valid one: their products only reach
+  // outputs that are never stored, and the loads stay unconditional (a load
+  // under a branch makes the compiler wait for every outstanding load where
+  // the branch rejoins, which would expose the prefetch latency each stage).
   const uint8_t* src[ROWS];
   const uint8_t* ssrc[ROWS];
-  bool ok[ROWS], isw[ROWS];
+  bool isw[ROWS];
   int lrow[ROWS];
 #pragma unroll
   for (int j = 0; j < ROWS; ++j) {
@@ -125,14 +129,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
     lrow[j] = row & 255;
     if (isw[j]) {
       const int wrow = n0 + row;
-      ok[j] = (wrow >> 4) < NT16;
-      src[j] = blob + wc_off + (int64_t(wrow >> 4) * KT * 16 + (wrow & 15)) * 64;
-      ssrc[j] = blob + ws_off + (int64_t(wrow >> 4) * KT * 16 + (wrow & 15)) * 8;
+      const int64_t wt = min(wrow >> 4, NT16 - 1);
+      src[j] = blob + wc_off + (wt * KT * 16 + (wrow & 15)) * 64;
+      ssrc[j] = blob + ws_off + (wt * KT * 16 + (wrow & 15)) * 8;
     } else {
-      const int xrow = m0 + row - 256;
-      ok[j] = xrow < M;
-      src[j] = xcodes + int64_t(xrow) * (K / 2);
-      ssrc[j] = xscales + int64_t(xrow) * (K / 16);
+      const int64_t xrow = min(m0 + row - 256, M - 1);
+      src[j] = xcodes + xrow * (K / 2);
+      ssrc[j] = xscales + xrow * (K / 16);
     }
   }
 
@@ -154,15 +157,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
         coff = int64_t(st) * 32;
         soff = int64_t(st) * 4;
       }
-      if (ok[j]) {
-        const uint4* p = reinterpret_cast<const uint4*>(src[j] + coff);
-        R.c[j][0] = p[0];
-        R.c[j][1] = p[1];
-        R.sc[j] = *reinterpret_cast<const uint32_t*>(ssrc[j] + soff);
-      } else {
-        R.c[j][0] = R.c[j][1] = make_uint4(0, 0, 0, 0);
-        R.sc[j] = 0;
-      }
+      const uint4* p = reinterpret_cast<const uint4*>(src[j] + coff);
+      R.c[j][0] = p[0];
+      R.c[j][1] = p[1];
+      R.sc[j] = *reinterpret_cast<const uint32_t*>(ssrc[j] + soff);
     }
   };
   // dequantize dword e (0 .. DW-1) of this thread's rows into LDS buffer buf
@@ -223,10 +221,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   for (int st = 0; st < S; st += 2) {
     // even stage: buffer 0; rb holds stage st+1; ra is free -> stage st+2
     gload(ra, min(st + 2, S - 1));
+    __builtin_amdgcn_sched_barrier(0);   // issue the prefetch here, not after the stage
     stage(0, rb);
     __syncthreads();
     // odd stage: buffer 1; ra holds stage st+2; rb is free -> stage st+3
     gload(rb, min(st + 3, S - 1));
+    __builtin_amdgcn_sched_barrier(0);
     stage(1, ra);
     __syncthreads();
   }
