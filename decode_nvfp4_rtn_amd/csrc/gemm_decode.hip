@@ -404,7 +404,7 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
   // per tile: each wave's partial sums go to one of two LDS slots (alternating
   // by tile, so one barrier per tile suffices); wave 0 adds them and stores
   __shared__ floatx4 red[2][KW][64];
-  auto finish = [&](const PersistTile<GW, kLut>& A, int t, int slot) {
+  auto finish = [&](const PersistTile<GW, kLut>& A, int t, int slot, bool store) {
     floatx4 tot;
     if constexpr (kLut) {
       floatx4 t2[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
     }
     red[slot][wave][lane] = tot;
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0 && store) {
       floatx4 v = red[slot][0][lane];
 #pragma unroll
       for (int w = 1; w < KW; ++w) v += red[slot][w][lane];
@@ -467,11 +467,19 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
   PersistTile<GW, kLut> A, B;
   int t = blockIdx.x;
   load(A, t);
+  // The second tile of an iteration may not exist (t + stride >= T): it is
+  // then computed from the clamped (valid) loads but not stored.  Keeping the
+  // arithmetic unconditional keeps the loop free of branches around waits,
+  // which would make the compiler wait for the in-flight prefetch as well.
+  // (the scheduling barriers keep each prefetch ahead of the arithmetic; the
+  // compiler would otherwise sink it below, to save registers)
   for (; t < T; t += 2 * stride) {
     load(B, min(t + stride, T - 1));
-    finish(A, t, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    finish(A, t, 0, true);
     load(A, min(t + 2 * stride, T - 1));
-    if (t + stride < T) finish(B, t + stride, 1);   // block-uniform condition
+    __builtin_amdgcn_sched_barrier(0);
+    finish(B, t + stride, 1, t + stride < T);
   }
 }
 
