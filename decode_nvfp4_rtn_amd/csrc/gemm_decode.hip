@@ -348,13 +348,20 @@ struct PersistTile<GW, true> {
 };
 
 // Blocks of this kernel that fit on one CU: two when the registers allow four
-// waves per SIMD (LUT2, or INT4 with two groups per wave), else one.
-constexpr int persist_blocks_per_cu(int gw, bool lut) { return (lut || gw == 2) ? 2 : 1; }
+// waves per SIMD (one m-tile with LUT2, or INT4 with two groups per wave),
+// else one.  With two m-tiles the block has 16 waves (four per SIMD).
+constexpr int persist_blocks_per_cu(int gw, int mt, bool lut) {
+  return mt == 1 && (lut || gw == 2) ? 2 : 1;
+}
+constexpr int persist_waves(int mt) { return mt == 1 ? KW : 2 * KW; }
 
-template <int GW, bool kLut, bool kBF16Out>
-__global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void decode_persist_kernel(
-    const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob, int64_t codes_off,
-    int64_t aux_off, int M, int N, int K, void* __restrict__ y) {
+template <int GW, int MT, bool kLut, bool kBF16Out>
+__global__ __launch_bounds__(persist_waves(MT) * 64,
+                             persist_waves(MT) / 4 * persist_blocks_per_cu(GW, MT, kLut))
+void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
+                           int64_t codes_off, int64_t aux_off, int M, int N, int K,
+                           void* __restrict__ y) {
+  constexpr int NW = persist_waves(MT);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
@@ -364,26 +371,31 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
 
-  const uint16_t* xr = x + int64_t(min(lane & 15, M - 1)) * K + 8 * (lane >> 4);
-  bf16x8_t xf[GW][4];
+  bf16x8_t xf[GW][4][MT];
 #pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    const int gc = min(g0 + i, G - 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
-      xf[i][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
-    }
-  }
-  floatx4 xs[GW];
-  if constexpr (!kLut) {
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 8 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
-      xs[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int gc = min(g0 + i, G - 1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        xs[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, xf[i][s], xs[i], 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
+        xf[i][s][mt] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+      }
     }
+  }
+  floatx4 xs[GW][MT];
+  if constexpr (!kLut) {
+#pragma unroll
+    for (int i = 0; i < GW; ++i)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        xs[i][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xs[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, xf[i][s][mt], xs[i][mt], 0, 0, 0);
+      }
   }
 
   auto load = [&](PersistTile<GW, kLut>& A, int t) {
@@ -403,11 +415,13 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
 
   // per tile: each wave's partial sums go to one of two LDS slots (alternating
   // by tile, so one barrier per tile suffices); wave 0 adds them and stores
-  __shared__ floatx4 red[2][KW][64];
+  __shared__ floatx4 red[2][NW][MT][64];
   auto finish = [&](const PersistTile<GW, kLut>& A, int t, int slot, bool store) {
-    floatx4 tot;
+    floatx4 tot[MT];
     if constexpr (kLut) {
-      floatx4 t2[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+      floatx4 t2[2][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) t2[0][mt] = t2[1][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const uint32_t keep = g0 + i < G ? 0xFFFFFFFFu : 0u;   // else zero codebook
@@ -417,46 +431,69 @@ __global__ __launch_bounds__(KW * 64, 2 * persist_blocks_per_cu(GW, kLut)) void 
         lut2_operands(A.w[i].y, lo, hi, a[2], a[3]);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          t2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], xf[i][s], t2[i & 1], 0, 0, 0);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            t2[i & 1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], xf[i][s][mt], t2[i & 1][mt], 0, 0, 0);
       }
-      tot = t2[0] + t2[1];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) tot[mt] = t2[0][mt] + t2[1][mt];
     } else {
-      floatx4 acc[GW];
+      // one m-tile: every group's MFMA chains first, then the scale
+      // arithmetic (no VALU waits on a fresh MFMA); two m-tiles: group by
+      // group, which needs fewer registers
+      constexpr int NA = MT == 1 ? GW : 1;
+      floatx4 acc[NA][MT];
 #pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        acc[i] = xs[i];
-        const uint32_t wd[4] = {A.w[i].x, A.w[i].y, A.w[i].z, A.w[i].w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4_operand(wd[s], nib_mask, bf16_128),
-                                                           xf[i][s], acc[i], 0, 0, 0);
-      }
-      tot = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
+      for (int mt = 0; mt < MT; ++mt) tot[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      auto scale_add = [&](int i, const floatx4 (&a)[MT]) {
         const bool live = g0 + i < G;
         const uint32_t s01 = live ? A.s[i].x : 0u, s23 = live ? A.s[i].y : 0u;
         const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
                              __uint_as_float(s23 << 16), __uint_as_float(s23 & 0xFFFF0000u)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tot[r] = fmaf(sc[r], acc[i][r], tot[r]);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tot[mt][r] = fmaf(sc[r], a[mt][r], tot[mt][r]);
+      };
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        floatx4 (&ai)[MT] = acc[MT == 1 ? i : 0];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) ai[mt] = xs[i][mt];
+        const uint32_t wd[4] = {A.w[i].x, A.w[i].y, A.w[i].z, A.w[i].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t op = int4_operand(wd[s], nib_mask, bf16_128);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            ai[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, xf[i][s][mt], ai[mt], 0, 0, 0);
+        }
+        if (MT != 1) scale_add(i, ai);
+      }
+      if (MT == 1) {
+#pragma unroll
+        for (int i = 0; i < GW; ++i) scale_add(i, acc[i]);
       }
     }
-    red[slot][wave][lane] = tot;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[slot][wave][mt][lane] = tot[mt];
     __syncthreads();
     if (wave == 0 && store) {
-      floatx4 v = red[slot][0][lane];
 #pragma unroll
-      for (int w = 1; w < KW; ++w) v += red[slot][w][lane];
-      const int n = t * 16 + 4 * (lane >> 4), m = lane & 15;
-      if (m < M) {
-        if (kBF16Out) {
-          uint2 o;
-          o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-          o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
-        } else {
-          *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+      for (int mt = 0; mt < MT; ++mt) {
+        floatx4 v = red[slot][0][mt][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[slot][w][mt][lane];
+        const int n = t * 16 + 4 * (lane >> 4), m = mt * 16 + (lane & 15);
+        if (m < M) {
+          if (kBF16Out) {
+            uint2 o;
+            o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+            o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
+          } else {
+            *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+          }
         }
       }
     }
@@ -572,20 +609,34 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
   // one m-tile, K <= 4096 and at least two row tiles per CU: persistent kernel
   const int G = static_cast<int>(k / 128);
   const int cus = device_cu_count();
-  if (m <= 16 && G <= KW * 4 && cus > 0 && n / 16 >= 2 * cus) {
+  // one pass over the batch (M <= 16; LUT2 also M <= 32), K <= 4096 and at
+  // least two row tiles per CU: persistent kernel.  (INT4 with two m-tiles
+  // would need more than the 128 registers that 16 waves per block allow.)
+  if ((m <= 16 || (kLut && m <= 32)) && G <= KW * 4 && cus > 0 && n / 16 >= 2 * cus) {
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const int M = int(m), N = int(n), K = int(k), T = int(n / 16);
-    auto run = [&](auto kern, int per_cu) {
+    auto run = [&](auto kern, int waves, int per_cu) {
       // every block must own at least two tiles, and the grid never exceeds T
       const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
-      kern<<<grid, KW * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M, N, K, y);
+      kern<<<grid, waves * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M, N, K, y);
       return hipGetLastError();
     };
-    if (G <= KW * 2)
-      return y_dtype == 1 ? run(decode_persist_kernel<2, kLut, true>, persist_blocks_per_cu(2, kLut))
-                          : run(decode_persist_kernel<2, kLut, false>, persist_blocks_per_cu(2, kLut));
-    return y_dtype == 1 ? run(decode_persist_kernel<4, kLut, true>, persist_blocks_per_cu(4, kLut))
-                        : run(decode_persist_kernel<4, kLut, false>, persist_blocks_per_cu(4, kLut));
+#define QL_PERSIST(GW, MT)                                                                 \
+    return y_dtype == 1                                                                   \
+               ? run(decode_persist_kernel<GW, MT, kLut, true>, persist_waves(MT),       \
+                     persist_blocks_per_cu(GW, MT, kLut))                                  \
+               : run(decode_persist_kernel<GW, MT, kLut, false>, persist_waves(MT),      \
+                     persist_blocks_per_cu(GW, MT, kLut))
+    if constexpr (kLut) {
+      if (m > 16) {
+        QL_PERSIST(2, 2);   // 16 waves: groups per wave <= 2 for K <= 4096
+      }
+    }
+    if (G <= KW * 2) {
+      QL_PERSIST(2, 1);
+    }
+    QL_PERSIST(4, 1);
+#undef QL_PERSIST
   }
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = static_cast<int>(m - m0 < 32 ? m - m0 : 32);

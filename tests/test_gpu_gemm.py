@@ -293,3 +293,33 @@ def test_decode_k_chunking(fmt, n, k):
         y = fn(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
         torch.cuda.synchronize()
         _check(host_f64(y)[:, cols], ref_fn(xb, *ref_w), False)
+
+
+# ----------------------------------------- persistent decode tile walk --
+# M <= 16 and K <= 4096 with at least two 16-row tiles per CU take the
+# persistent kernel: each block walks tiles blockIdx.x, + gridDim.x, ...
+# These shapes give an odd number of tiles per block (a last tile without a
+# partner), a group count that leaves the last wave partly idle (K = 3840:
+# 30 groups over 8 waves of 4) and the two-groups-per-wave variant (K = 2048).
+
+@pytest.mark.parametrize("fmt", ["int4", "lut2"])
+@pytest.mark.parametrize("n,k", [(16 * 1031, 3840), (16 * 1537, 2048)])
+def test_decode_persistent_tile_walk(fmt, n, k):
+    q = require_gpu()
+    w = synth.weights(10, k, n, k)
+    say("decode persistent", fmt, n, k)
+    cols = np.unique(np.concatenate([sample_rows(n, 96, n + 7 * k), np.arange(n - 48, n)]))
+    if fmt == "int4":
+        blob = _int4_blob(q, w)
+        ref_w = int4.quantize(w[cols])
+        fn, ref_fn = q.gemm_w4a16, gemm.w4a16
+    else:
+        blob = _lut2_blob(q, w)
+        ref_w = lut2.fit(w[cols])
+        fn, ref_fn = q.gemm_lut2, gemm.lut2_gemm
+    del w
+    for m in (1, 7, 16):
+        xb = synth.activations_bf16(10, m, m, k)
+        y = fn(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(host_f64(y)[:, cols], ref_fn(xb, *ref_w), False)
