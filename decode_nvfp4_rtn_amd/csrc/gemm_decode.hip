@@ -325,6 +325,126 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
   reduce_store<MT, NTB, KWT, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
+// Pipelined k-split variant for one m-tile (M <= 16) and long K (at least
+// two chunks of W groups per wave): a block of 8 waves owns one row tile and
+// the waves split k, as above, but each wave walks its groups in chunks of W
+// with the next chunk's loads in flight while it computes the current one
+// (two register sets).  A chunk's activation fragments travel in the same
+// batch as its weights: loads complete in issue order for the wait counter,
+// so fragments fetched later would make the arithmetic wait for the next
+// chunk's weights as well.
+template <int W, bool kLut>
+struct PipeBatch;
+template <int W>
+struct PipeBatch<W, false> {
+  uint4 w[W];
+  uint2 s[W];
+  bf16x8_t x[W][4];
+};
+template <int W>
+struct PipeBatch<W, true> {
+  uint2 w[W];
+  bf16x8_t x[W][4];
+};
+
+template <int W, bool kLut, bool kBF16Out>
+__global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob, int64_t codes_off,
+    int64_t aux_off, int M, int N, int K, void* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int G = K / 128;
+  const int gpw = (G + KW - 1) / KW;
+  const int g0 = wave * gpw;
+  const int64_t tile = blockIdx.x;
+  const uint32_t m136 = vconst(0xC308C308u);
+  const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
+  const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
+  const uint16_t* xr = x + int64_t(min(lane & 15, M - 1)) * K + 8 * (lane >> 4);
+  uint32_t lo_t = 0, hi_t = 0;
+  if constexpr (kLut) {
+    const uint2 b = reinterpret_cast<const uint2*>(blob + aux_off)[tile * 16 + (lane & 15)];
+    lo_t = b.x;
+    hi_t = b.y;
+  }
+
+  auto load = [&](PipeBatch<W, kLut>& B, int c0) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int gc = min(g0 + min(c0 + i, gpw - 1), G - 1);
+      const int64_t gi = tile * G + gc;
+      if constexpr (kLut) {
+        B.w[i] = load_nt8(reinterpret_cast<const uint2*>(blob + codes_off) + gi * 64 + lane);
+      } else {
+        B.w[i] = load_nt16(reinterpret_cast<const uint4*>(blob + codes_off) + gi * 64 + lane);
+        B.s[i] = reinterpret_cast<const uint2*>(blob + aux_off)[gi * 4 + (lane >> 4)];
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
+        B.x[i][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+      }
+    }
+  };
+
+  floatx4 tot[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  auto compute = [&](const PipeBatch<W, kLut>& B, int c0) {
+    if constexpr (kLut) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const int g = g0 + c0 + i;
+        const uint32_t keep = (c0 + i < gpw && g < G) ? 0xFFFFFFFFu : 0u;   // else zero codebook
+        bf16x8_t a[4];
+        lut2_operands(B.w[i].x, lo_t & keep, hi_t & keep, a[0], a[1]);
+        lut2_operands(B.w[i].y, lo_t & keep, hi_t & keep, a[2], a[3]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          tot[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], B.x[i][s], tot[i & 1], 0, 0, 0);
+      }
+    } else {
+      floatx4 acc[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, B.x[i][s], acc[i], 0, 0, 0);
+        const uint32_t wd[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4_operand(wd[s], nib_mask, bf16_128),
+                                                           B.x[i][s], acc[i], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < W; ++i) {
+        const bool live = c0 + i < gpw && g0 + c0 + i < G;
+        const uint32_t s01 = live ? B.s[i].x : 0u, s23 = live ? B.s[i].y : 0u;
+        const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
+                             __uint_as_float(s23 << 16), __uint_as_float(s23 & 0xFFFF0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[0][r] = fmaf(sc[r], acc[i][r], tot[0][r]);
+      }
+    }
+  };
+
+  // (the scheduling barriers keep each batch's loads ahead of the arithmetic
+  // on the previous one; the compiler would otherwise sink them below it)
+  PipeBatch<W, kLut> A, B;
+  load(A, 0);
+  int c0 = 0;
+  for (; c0 + W < gpw; c0 += 2 * W) {   // chunks c0 (in A) and c0 + W (in B)
+    load(B, c0 + W);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(A, c0);
+    load(A, c0 + 2 * W);                 // clamped when past the range
+    __builtin_amdgcn_sched_barrier(0);
+    compute(B, c0 + W);
+  }
+  if (c0 < gpw) compute(A, c0);          // wave-uniform: an odd last chunk
+  floatx4 t1[1][1] = {{tot[0] + tot[1]}};
+  reduce_store<1, 1, KW, kBF16Out>(t1, int(tile), 0, M, N, y);
+}
+
 // Persistent variant for one m-tile (M <= 16) and K <= 128 * KW * GW.  Wave w
 // owns groups [GW w, GW w + GW) of every row tile, so its activation
 // fragments -- and, for INT4, the -136 * sum x seeds -- are the same for all
@@ -637,6 +757,29 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
     }
     QL_PERSIST(4, 1);
 #undef QL_PERSIST
+  }
+  // one m-tile, one row tile per block and long K: pipelined k-split kernel
+  const int gpw8 = (G + KW - 1) / KW;
+  if (m <= 16 && !wide && gpw8 >= 8) {
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const int M = int(m), N = int(n), K = int(k), T = int(n / 16);
+    // chunks of 4 groups (LUT2: 5 when that makes three chunks, no padding)
+    const bool w5 = kLut && gpw8 > 12 && gpw8 <= 15;
+#define QL_PIPE(W)                                                                          \
+    {                                                                                      \
+      if (y_dtype == 1)                                                                    \
+        decode_pipe_kernel<W, kLut, true><<<T, KW * 64, 0, s>>>(xp, blob, L.codes_off,     \
+                                                               L.aux_off, M, N, K, y);     \
+      else                                                                                 \
+        decode_pipe_kernel<W, kLut, false><<<T, KW * 64, 0, s>>>(xp, blob, L.codes_off,    \
+                                                                L.aux_off, M, N, K, y);    \
+      return hipGetLastError();                                                            \
+    }
+    if constexpr (kLut) {
+      if (w5) QL_PIPE(5)
+    }
+    QL_PIPE(4)
+#undef QL_PIPE
   }
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = static_cast<int>(m - m0 < 32 ? m - m0 : 32);
