@@ -318,8 +318,37 @@ def test_decode_persistent_tile_walk(fmt, n, k):
         ref_w = lut2.fit(w[cols])
         fn, ref_fn = q.gemm_lut2, gemm.lut2_gemm
     del w
-    for m in (1, 7, 16):
+    for m in (1, 7, 16, 25):   # 25: LUT2 takes the two-m-tile persistent kernel
         xb = synth.activations_bf16(10, m, m, k)
         y = fn(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
         torch.cuda.synchronize()
         _check(host_f64(y)[:, cols], ref_fn(xb, *ref_w), False)
+
+
+# ------------------------------------------ cooperative W4A4, ragged edges --
+# Problems with at least 256 tiles of 256 x 256 take the block-cooperative
+# kernel.  With M and N not multiples of 256 its edge blocks read clamped
+# (last valid) rows for the rows past M or N; those products must reach no
+# stored output.  Checked on the last rows and columns and a sample.
+
+@pytest.mark.parametrize("m,n,k", [(4100, 16400, 512), (8191, 8208, 640)])
+def test_w4a4_cooperative_ragged_edges(m, n, k):
+    q = require_gpu()
+    assert ((m + 255) // 256) * ((n + 255) // 256) >= 256
+    bits = synth.activations_bf16(11, m, m, k, outliers="channels")
+    w = synth.weights(11, n, n, k)
+    say("w4a4 coop ragged", m, n, k)
+    blob = _nvfp4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_bf16(bits))
+    y32 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.float32)
+    y16 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(m, 40, m + 3), np.arange(m - 24, m)]))
+    cols = np.unique(np.concatenate([sample_rows(n, 40, n + 5), np.arange(n - 24, n)]))
+    xf = synth.bf16_bits_as_f32(bits)
+    ref = gemm.w4a4(*nvfp4.quantize(xf[rows], s_t=nvfp4.tensor_scale(xf)),
+                    *nvfp4.quantize(w[cols], s_t=nvfp4.tensor_scale(w)))
+    _check(host_f64(y32)[np.ix_(rows, cols)], ref, False)
+    _check(host_f64(y16)[np.ix_(rows, cols)], ref, True)
+    # nothing was written past the output: the buffers are exactly [m, n]
+    assert y32.shape == (m, n) and y16.shape == (m, n)
