@@ -68,7 +68,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-reps", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=256,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of X per layer in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-sweep", action="store_true")
