@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-sweep", action="store_true")
     ap.add_argument("--no-bf16-reference", action="store_true")
+    ap.add_argument("--no-odp", action="store_true",
+                    help="skip the host-to-device weight streaming measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 device copies of 256 MiB (a kernel of known traffic, "
                          "to scale the FETCH_SIZE/WRITE_SIZE counters of a --pmc run)")
@@ -269,6 +271,85 @@ def main():
                 out[f"m{m}"] = round(float(np.mean([v["gbps"] for v in vals])), 1)
         return out
 
+    # -------------------------------- weight streaming from host (ODP) ----
+    # A layer block's packed weights (the four prefill layers) stream from
+    # pinned host memory through two device buffers while the previous block
+    # is quantized and multiplied (decode_nvfp4_rtn_amd.pipeline); a stack of
+    # ODP_BLOCKS blocks with these weights is run.  Per batch size M: time of
+    # the stack with resident weights, of the block copies alone, and of the
+    # streamed stack; `exposed` is what the copies add.
+    odp = {}
+    if not args.no_odp:
+        from decode_nvfp4_rtn_amd.pipeline import PrefillWeightStream
+        ODP_BLOCKS = 4
+        host = [p["blob"].cpu().pin_memory() for p in P]
+        streamer = PrefillWeightStream([host], dev)
+        wbytes = float(sum(h.numel() for h in host))
+        shapes = [(p["L"].n, p["L"].k) for p in P]
+
+        def timed(fn, stream=None, reps=5):
+            out = []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                a, b = E(enable_timing=True), E(enable_timing=True)
+                st = stream if stream is not None else torch.cuda.current_stream()
+                a.record(st)
+                fn()
+                b.record(st)
+                torch.cuda.synchronize()
+                out.append(a.elapsed_time(b))
+            return float(np.median(out))
+
+        def copies_alone():
+            with torch.cuda.stream(streamer.copy_stream):
+                for blk in range(ODP_BLOCKS):
+                    for j, h in enumerate(host):
+                        streamer._blob(blk % 2, 0, j).copy_(h, non_blocking=True)
+
+        copy_ms = timed(copies_alone, stream=streamer.copy_stream)
+        for m_odp in (512, 1024, 2048, 4096, 8192):
+            xs = [p["x"][:m_odp] for p in P]
+            cs = [p["codes"][:m_odp] for p in P]
+            ss = [p["scales"][:m_odp] for p in P]
+            ts = [p["ts"] for p in P]
+            ws = [p["ws"] for p in P]
+            ys = [p["y"][:m_odp] for p in P]
+
+            def resident():
+                for _ in range(ODP_BLOCKS):
+                    for i, p in enumerate(P):
+                        qlin.quantize_nvfp4(xs[i], codes=cs[i], scales=ss[i], workspace=ws[i],
+                                            ts_out=ts[i])
+                        qlin.gemm_w4a4(cs[i], ss[i], ts[i], p["blob"], m_odp, p["L"].n,
+                                       p["L"].k, y=ys[i])
+
+            comp_ms = timed(resident)
+            strm_ms = timed(lambda: streamer.run([0] * ODP_BLOCKS, shapes, xs, ys, cs, ss, ts, ws))
+            exposed = max(strm_ms - comp_ms, 0.0)
+            # the first block's copy cannot overlap anything (pipeline fill)
+            steady = max(strm_ms - comp_ms - copy_ms / ODP_BLOCKS, 0.0)
+            odp[f"m{m_odp}"] = {"compute_ms": round(comp_ms, 4), "streamed_ms": round(strm_ms, 4),
+                                "exposed_ms": round(exposed, 4),
+                                "exposed_after_fill_ms": round(steady, 4),
+                                "hidden_frac": round(1.0 - min(exposed / copy_ms, 1.0), 3),
+                                "block_compute_ms": round(comp_ms / ODP_BLOCKS, 4)}
+            _progress(f"odp m={m_odp}: compute {comp_ms:.3f} ms, streamed {strm_ms:.3f} ms")
+        # batch size at which one block's compute equals one block's copy
+        # (linear interpolation between the measured sizes)
+        per_copy = copy_ms / ODP_BLOCKS
+        ms_sorted = sorted(int(k[1:]) for k in odp)
+        cross = None
+        for a_m, b_m in zip(ms_sorted, ms_sorted[1:]):
+            ca, cb = odp[f"m{a_m}"]["block_compute_ms"], odp[f"m{b_m}"]["block_compute_ms"]
+            if ca < per_copy <= cb:
+                cross = round(a_m + (per_copy - ca) * (b_m - a_m) / (cb - ca))
+        odp["m_where_block_compute_equals_block_copy"] = cross
+        odp["blocks"] = ODP_BLOCKS
+        odp["copy_ms"] = round(copy_ms, 4)
+        odp["h2d_gbps"] = round(ODP_BLOCKS * wbytes / copy_ms / 1e6, 1)
+        odp["block_weights_mb"] = round(wbytes / 1e6, 1)
+        del streamer, host
+
     # ------------------------------------------- BF16 reference points ----
     # The pages state their speed-ups against BF16; torch's bf16 matmul
     # (hipBLASLt) on the same shapes is that reference here: prefill
@@ -384,6 +465,7 @@ def main():
             "lut2_gbps_mean_over_layers": _agg("lut2", lut.ms),
             "decode_sweep": sweep,
             "bf16_reference": bf16_ref,
+            "odp_weight_streaming": odp,
             "w4a4_gemm_speedup_vs_bf16": (
                 round(sum(v["us"] for k, v in bf16_ref.items() if k.startswith("prefill/"))
                       / (gemm_ms_step * 1e3), 3) if bf16_ref else None),
