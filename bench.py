@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-sweep", action="store_true")
     ap.add_argument("--no-bf16-reference", action="store_true")
+    ap.add_argument("--no-27b", action="store_true",
+                    help="skip the 27B-class prefill measurement (M = 4096, 16384, 32768)")
     ap.add_argument("--no-odp", action="store_true",
                     help="skip the host-to-device weight streaming measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -350,6 +352,78 @@ def main():
         odp["block_weights_mb"] = round(wbytes / 1e6, 1)
         del streamer, host
 
+    # ------------------------------- 27B-class long-context prefill ----
+    # NVFP4 W4A4 prefill (quantize + GEMM, bf16 out) of the 27B-class layer
+    # set at M = 4096, 16384 and 32768 tokens, interleaved round-robin over
+    # sizes and layers in this one process.  Activations: the first 4096 rows
+    # of each layer's seeded draw (N(0,1), 0.1 % of elements x50, bf16),
+    # repeated down to M rows (timing does not depend on the values; drawing
+    # 1.1 G values on the host would take longer than the whole measurement).
+    big = {}
+    if not args.no_27b:
+        b27 = configs.BIG27_PREFILL
+        MB = max(b27.ms)
+        R = []
+        for li, L in enumerate(b27.layers):
+            x0 = bf16(synth.activations_bf16(b27.cid, li, 4096, L.k, outliers=b27.outliers))
+            x = x0.repeat(MB // 4096, 1)
+            del x0
+            wc, ws, wt = qlin.quantize_nvfp4(f32(synth.weights(b27.cid, li, L.n, L.k)))
+            blob = qlin.repack_weights(qlin.QL_NVFP4, L.n, L.k, wc, ws, wt)
+            del wc, ws
+            R.append(dict(L=L, x=x, blob=blob,
+                          codes=torch.empty((MB, L.k // 2), dtype=torch.uint8, device=dev),
+                          scales=torch.empty((MB, L.k // 16), dtype=torch.uint8, device=dev),
+                          ts=torch.empty(1, dtype=torch.float32, device=dev),
+                          ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(MB, L.k)),
+                                         dtype=torch.uint8, device=dev),
+                          y=torch.empty((MB, L.n), dtype=torch.bfloat16, device=dev)))
+        torch.cuda.synchronize()
+        _progress("27B-class inputs and packed weights resident")
+        reps = 5
+        tq = {(m, i): [] for m in b27.ms for i in range(len(R))}
+        tg = {(m, i): [] for m in b27.ms for i in range(len(R))}
+        for rep in range(reps + 1):
+            for m in b27.ms:
+                for i, r in enumerate(R):
+                    L = r["L"]
+                    e0, e1, e2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
+                    e0.record()
+                    qlin.quantize_nvfp4(r["x"][:m], codes=r["codes"][:m], scales=r["scales"][:m],
+                                        workspace=r["ws"], ts_out=r["ts"])
+                    e1.record()
+                    qlin.gemm_w4a4(r["codes"][:m], r["scales"][:m], r["ts"], r["blob"], m, L.n, L.k,
+                                   y=r["y"][:m])
+                    e2.record()
+                    if rep > 0:   # the first round is a warm-up
+                        tq[(m, i)].append((e0, e1))
+                        tg[(m, i)].append((e1, e2))
+        torch.cuda.synchronize()
+        for m in b27.ms:
+            rows, fl_all, q_all, g_all = [], 0.0, 0.0, 0.0
+            for i, r in enumerate(R):
+                L = r["L"]
+                q = float(np.median([a.elapsed_time(b) for a, b in tq[(m, i)]]))
+                g = float(np.median([a.elapsed_time(b) for a, b in tg[(m, i)]]))
+                fl = 2.0 * m * L.n * L.k
+                fl_all, q_all, g_all = fl_all + fl, q_all + q, g_all + g
+                rows.append({"layer": L.name, "n": L.n, "k": L.k, "gemm_us": round(g * 1e3, 1),
+                             "gemm_tflops": round(fl / g / 1e9, 1), "quantize_us": round(q * 1e3, 1)})
+            big[f"m{m}"] = {
+                "layers": rows,
+                "gemm_tflops": round(fl_all / g_all / 1e9, 1),
+                "prefill_tflops_incl_quantize": round(fl_all / (g_all + q_all) / 1e9, 1),
+                "gemm_frac_f16_peak": round(fl_all / g_all / 1e9 / PEAK["f16"], 4),
+                "gemm_frac_fp8_peak": round(fl_all / g_all / 1e9 / PEAK["fp8"], 4),
+                "gemm_frac_fp4_peak": round(fl_all / g_all / 1e9 / PEAK["fp4"], 4),
+                "quantize_ms": round(q_all, 4), "gemm_ms": round(g_all, 4)}
+            _progress(f"27b m={m}: GEMM {big[f'm{m}']['gemm_tflops']} TFLOP/s, "
+                      f"with quantize {big[f'm{m}']['prefill_tflops_incl_quantize']}")
+        big["activations"] = ("first 4096 rows of each layer's seeded draw repeated to M rows; "
+                              "median of 5 interleaved rounds after one warm-up round")
+        del R
+        torch.cuda.empty_cache()
+
     # ------------------------------------------- BF16 reference points ----
     # The pages state their speed-ups against BF16; torch's bf16 matmul
     # (hipBLASLt) on the same shapes is that reference here: prefill
@@ -466,6 +540,7 @@ def main():
             "decode_sweep": sweep,
             "bf16_reference": bf16_ref,
             "odp_weight_streaming": odp,
+            "prefill_27b": big,
             "w4a4_gemm_speedup_vs_bf16": (
                 round(sum(v["us"] for k, v in bf16_ref.items() if k.startswith("prefill/"))
                       / (gemm_ms_step * 1e3), 3) if bf16_ref else None),
