@@ -40,6 +40,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int KW = 8;  // wavefronts per block (k split)
 
@@ -445,15 +446,24 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
   reduce_store<1, 1, KW, kBF16Out>(t1, int(tile), 0, M, N, y);
 }
 
-// Persistent variant for one m-tile (M <= 16) and K <= 128 * KW * GW.  Wave w
-// owns groups [GW w, GW w + GW) of every row tile, so its activation
-// fragments -- and, for INT4, the -136 * sum x seeds -- are the same for all
-// tiles: they are loaded and computed once per wave and stay in registers.
-// One or two blocks per CU walk the row tiles t = blockIdx.x, + gridDim.x, ...
-// with the next tile's weights (two register sets) in flight while the
-// current one is dequantized, multiplied and reduced; no activation load sits
-// between them in the load queue, so the arithmetic waits only for its own
-// tile.  Used when every block gets at least two tiles.
+// Persistent variant for M <= 32 and K <= 128 * KW * GW.  Wave w owns groups
+// [GW w, GW w + GW) of every row tile, so its activation fragments -- and, for
+// INT4, the -136 * sum x seeds -- are the same for all tiles: they are loaded
+// and computed once per wave.  One or two blocks per CU walk the row tiles
+// t = blockIdx.x, + gridDim.x, ... with the next tile's weights (two register
+// sets) in flight while the current one is dequantized, multiplied and
+// reduced; no activation load sits between them in the load queue, so the
+// arithmetic waits only for its own tile.  Used when every block gets at
+// least two tiles.
+//
+// Weights are read through a buffer resource made per tile, so tile and group
+// offsets are scalar and no vector instruction computes an address.  The
+// first tile's loads are issued before the seed MFMAs (which wait only for
+// the activation loads ahead of them).  The eight (sixteen) partial sums of a
+// tile are added by four (eight) waves at once, one accumulator component
+// each.  INT4 with two m-tiles keeps the second m-tile's fragments in LDS
+// (lane-private, so they need no barrier): in registers they would not fit
+// next to the two weight sets at two waves per SIMD.
 template <int GW, bool kLut>
 struct PersistTile;
 template <int GW>
@@ -467,31 +477,84 @@ struct PersistTile<GW, true> {
   uint2 book;
 };
 
+// waves per block: 8, or 16 for LUT2 with two m-tiles (two groups per wave)
+constexpr int persist_waves(int mt, bool lut) { return mt == 2 && lut ? 2 * KW : KW; }
 // Blocks of this kernel that fit on one CU: two when the registers allow four
 // waves per SIMD (one m-tile with LUT2, or INT4 with two groups per wave),
-// else one.  With two m-tiles the block has 16 waves (four per SIMD).
+// else one.
 constexpr int persist_blocks_per_cu(int gw, int mt, bool lut) {
   return mt == 1 && (lut || gw == 2) ? 2 : 1;
 }
-constexpr int persist_waves(int mt) { return mt == 1 ? KW : 2 * KW; }
+constexpr bool persist_x_in_lds(int mt, bool lut) { return mt == 2 && !lut; }
+// dynamic LDS: two reduction slots [2][waves][MT][4][64] floats, then (INT4,
+// two m-tiles) the second m-tile's fragments [waves][GW][4][64] x 16 bytes
+constexpr size_t persist_red_bytes(int mt, bool lut) {
+  return size_t(2) * persist_waves(mt, lut) * mt * 4 * 64 * 4;
+}
+constexpr size_t persist_lds_bytes(int gw, int mt, bool lut) {
+  return persist_red_bytes(mt, lut) +
+         (persist_x_in_lds(mt, lut) ? size_t(persist_waves(mt, lut)) * gw * 4 * 64 * 16 : 0);
+}
+
+// Buffer resource word 3 for raw 32-bit buffer loads, and the non-temporal
+// cache policy for streamed weights.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kPolicyNT = 2;
 
 template <int GW, int MT, bool kLut, bool kBF16Out>
-__global__ __launch_bounds__(persist_waves(MT) * 64,
-                             persist_waves(MT) / 4 * persist_blocks_per_cu(GW, MT, kLut))
+__global__ __launch_bounds__(persist_waves(MT, kLut) * 64,
+                             persist_waves(MT, kLut) / 4 * persist_blocks_per_cu(GW, MT, kLut))
 void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                            int64_t codes_off, int64_t aux_off, int M, int N, int K,
                            void* __restrict__ y) {
-  constexpr int NW = persist_waves(MT);
+  constexpr int NW = persist_waves(MT, kLut);
+  constexpr bool kXL = persist_x_in_lds(MT, kLut);
+  constexpr int MR = kXL ? 1 : MT;         // m-tiles whose fragments stay in registers
+  constexpr int CB = kLut ? 512 : 1024;    // code bytes per (row tile, group)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const red = reinterpret_cast<float*>(smem);
+  bf16x8_t* const xl = reinterpret_cast<bf16x8_t*>(smem + persist_red_bytes(MT, kLut));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
   const int g0 = wave * GW;
   const int T = N / 16;
+  const int stride = gridDim.x;
   const uint32_t m136 = vconst(0xC308C308u);
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
 
-  bf16x8_t xf[GW][4][MT];
+  auto load = [&](PersistTile<GW, kLut>& A, int t) {
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(blob + codes_off + int64_t(t) * G * CB), 0, G * CB, kRsrcWord3);
+    if constexpr (kLut) {
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rc, lane * 8, min(g0 + i, G - 1) * CB,
+                                                             kPolicyNT);
+        A.w[i] = make_uint2(v[0], v[1]);
+      }
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(blob + aux_off + int64_t(t) * 128), 0, 128, kRsrcWord3);
+      const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(rb, (lane & 15) * 8, 0, 0);
+      A.book = make_uint2(b[0], b[1]);
+    } else {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(blob + aux_off + int64_t(t) * G * 32), 0, G * 32, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const int gc = min(g0 + i, G - 1);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16, gc * CB, kPolicyNT);
+        A.w[i] = make_uint4(v[0], v[1], v[2], v[3]);
+        const u32x2 s = __builtin_amdgcn_raw_buffer_load_b64(rs, (lane >> 4) * 8, gc * 32, 0);
+        A.s[i] = make_uint2(s[0], s[1]);
+      }
+    }
+  };
+
+  // activation fragments (issued first), then the first tile's weights
+  bf16x8_t xf[GW][4][MR];
+  bf16x8_t xt[kXL ? GW : 1][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 8 * (lane >> 4);
@@ -501,10 +564,18 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
-        xf[i][s][mt] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+        if (kXL && mt == 1)
+          xt[kXL ? i : 0][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+        else
+          xf[i][s][mt < MR ? mt : 0] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
       }
     }
   }
+  PersistTile<GW, kLut> A, B;
+  int t = blockIdx.x;
+  load(A, t);
+  __builtin_amdgcn_sched_barrier(0);   // keep the tile loads ahead of the seed arithmetic
+
   floatx4 xs[GW][MT];
   if constexpr (!kLut) {
 #pragma unroll
@@ -514,30 +585,22 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
         xs[i][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          xs[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, xf[i][s][mt], xs[i][mt], 0, 0, 0);
+          xs[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              neg136, (kXL && mt == 1) ? xt[kXL ? i : 0][s] : xf[i][s][mt < MR ? mt : 0],
+              xs[i][mt], 0, 0, 0);
       }
   }
-
-  auto load = [&](PersistTile<GW, kLut>& A, int t) {
+  if constexpr (kXL) {
 #pragma unroll
-    for (int i = 0; i < GW; ++i) {
-      const int64_t gi = int64_t(t) * G + min(g0 + i, G - 1);
-      if constexpr (kLut) {
-        A.w[i] = load_nt8(reinterpret_cast<const uint2*>(blob + codes_off) + gi * 64 + lane);
-      } else {
-        A.w[i] = load_nt16(reinterpret_cast<const uint4*>(blob + codes_off) + gi * 64 + lane);
-        A.s[i] = reinterpret_cast<const uint2*>(blob + aux_off)[gi * 4 + (lane >> 4)];
-      }
-    }
-    if constexpr (kLut)
-      A.book = reinterpret_cast<const uint2*>(blob + aux_off)[int64_t(t) * 16 + (lane & 15)];
-  };
+    for (int i = 0; i < GW; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xl[((wave * GW + i) * 4 + s) * 64 + lane] = xt[i][s];
+  }
 
-  // per tile: each wave's partial sums go to one of two LDS slots (alternating
-  // by tile, so one barrier per tile suffices); wave 0 adds them and stores
-  __shared__ floatx4 red[2][NW][MT][64];
   auto finish = [&](const PersistTile<GW, kLut>& A, int t, int slot, bool store) {
     floatx4 tot[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) tot[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if constexpr (kLut) {
       floatx4 t2[2][MT];
 #pragma unroll
@@ -558,14 +621,28 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) tot[mt] = t2[0][mt] + t2[1][mt];
     } else {
-      // one m-tile: every group's MFMA chains first, then the scale
-      // arithmetic (no VALU waits on a fresh MFMA); two m-tiles: group by
-      // group, which needs fewer registers
-      constexpr int NA = MT == 1 ? GW : 1;
-      floatx4 acc[NA][MT];
+      // every group's MFMA chains first, then the fp32 scale arithmetic, so
+      // no VALU instruction waits on an MFMA it has just issued
+      floatx4 acc[GW][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) tot[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      auto scale_add = [&](int i, const floatx4 (&a)[MT]) {
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[i][mt] = xs[i][mt];
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const uint32_t wd[4] = {A.w[i].x, A.w[i].y, A.w[i].z, A.w[i].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8_t op = int4_operand(wd[s], nib_mask, bf16_128);
+          acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, xf[i][s][0], acc[i][0], 0, 0, 0);
+          if constexpr (MT == 2)
+            acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                op, kXL ? xl[((wave * GW + i) * 4 + s) * 64 + lane] : xf[i][s][MR - 1], acc[i][1],
+                0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
         const bool live = g0 + i < G;
         const uint32_t s01 = live ? A.s[i].x : 0u, s23 = live ? A.s[i].y : 0u;
         const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
@@ -573,57 +650,36 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tot[mt][r] = fmaf(sc[r], a[mt][r], tot[mt][r]);
-      };
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
-        floatx4 (&ai)[MT] = acc[MT == 1 ? i : 0];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) ai[mt] = xs[i][mt];
-        const uint32_t wd[4] = {A.w[i].x, A.w[i].y, A.w[i].z, A.w[i].w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_t op = int4_operand(wd[s], nib_mask, bf16_128);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            ai[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op, xf[i][s][mt], ai[mt], 0, 0, 0);
-        }
-        if (MT != 1) scale_add(i, ai);
-      }
-      if (MT == 1) {
-#pragma unroll
-        for (int i = 0; i < GW; ++i) scale_add(i, acc[i]);
+          for (int r = 0; r < 4; ++r) tot[mt][r] = fmaf(sc[r], acc[i][mt][r], tot[mt][r]);
       }
     }
+    // partial sums -> LDS slot; 4 * MT waves each add one component
+    float* rs = red + size_t(slot) * NW * MT * 4 * 64;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) red[slot][wave][mt][lane] = tot[mt];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rs[((wave * MT + mt) * 4 + r) * 64 + lane] = tot[mt][r];
     __syncthreads();
-    if (wave == 0 && store) {
+    if (wave < 4 * MT && store) {
+      const int mt = wave >> 2, r = wave & 3;
+      float v[NW];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        floatx4 v = red[slot][0][mt][lane];
+      for (int w = 0; w < NW; ++w) v[w] = rs[((w * MT + mt) * 4 + r) * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[slot][w][mt][lane];
-        const int n = t * 16 + 4 * (lane >> 4), m = mt * 16 + (lane & 15);
-        if (m < M) {
-          if (kBF16Out) {
-            uint2 o;
-            o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-            o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
-          } else {
-            *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
-          }
-        }
+      for (int h = NW / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int w = 0; w < h; ++w) v[w] += v[w + h];
+      const int m = mt * 16 + (lane & 15), n = t * 16 + 4 * (lane >> 4) + r;
+      if (m < M) {
+        if (kBF16Out)
+          static_cast<uint16_t*>(y)[int64_t(m) * N + n] = uint16_t(f32_to_bf16_rne(v[0]));
+        else
+          static_cast<float*>(y)[int64_t(m) * N + n] = v[0];
       }
     }
   };
 
-  // the launch guarantees gridDim.x <= T, so every block has a first tile
-  const int stride = gridDim.x;
-  PersistTile<GW, kLut> A, B;
-  int t = blockIdx.x;
-  load(A, t);
+  // the launch guarantees gridDim.x <= T, so every block has a first tile.
   // The second tile of an iteration may not exist (t + stride >= T): it is
   // then computed from the clamped (valid) loads but not stored.  Keeping the
   // arithmetic unconditional keeps the loop free of branches around waits,
@@ -638,6 +694,19 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
     __builtin_amdgcn_sched_barrier(0);
     finish(B, t + stride, 1, t + stride < T);
   }
+}
+
+// The dynamic-LDS limit is a per-function attribute: raised once per
+// instantiation that needs more than the default 64 KiB.
+template <int GW, int MT, bool kLut, bool kBF16Out>
+hipError_t persist_lds_attr() {
+  static const hipError_t e =
+      persist_lds_bytes(GW, MT, kLut) > 65536
+          ? hipFuncSetAttribute(
+                reinterpret_cast<const void*>(decode_persist_kernel<GW, MT, kLut, kBF16Out>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, int(persist_lds_bytes(GW, MT, kLut)))
+          : hipSuccess;
+  return e;
 }
 
 template <bool kLut, int MT, int NTB, int WMAX, int KWT>
@@ -726,30 +795,34 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
   // two row tiles per block when there are enough tiles to keep every CU busy
   // (N >= 6144 gives at least 192 blocks of 512 threads)
   const bool wide = n / 16 >= 384;
-  // one m-tile, K <= 4096 and at least two row tiles per CU: persistent kernel
   const int G = static_cast<int>(k / 128);
   const int cus = device_cu_count();
-  // one pass over the batch (M <= 16; LUT2 also M <= 32), K <= 4096 and at
-  // least two row tiles per CU: persistent kernel.  (INT4 with two m-tiles
-  // would need more than the 128 registers that 16 waves per block allow.)
-  if ((m <= 16 || (kLut && m <= 32)) && G <= KW * 4 && cus > 0 && n / 16 >= 2 * cus) {
+  // one pass over the batch (M <= 32), K <= 4096 and at least two row tiles
+  // per CU: persistent kernel
+  if (m <= 32 && G <= KW * 4 && cus > 0 && n / 16 >= 2 * cus) {
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const int M = int(m), N = int(n), K = int(k), T = int(n / 16);
-    auto run = [&](auto kern, int waves, int per_cu) {
+    auto run = [&](auto kern, int waves, int per_cu, size_t lds, hipError_t attr) {
+      if (attr != hipSuccess) return attr;
       // every block must own at least two tiles, and the grid never exceeds T
       const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
-      kern<<<grid, waves * 64, 0, s>>>(xp, blob, L.codes_off, L.aux_off, M, N, K, y);
+      kern<<<grid, waves * 64, lds, s>>>(xp, blob, L.codes_off, L.aux_off, M, N, K, y);
       return hipGetLastError();
     };
-#define QL_PERSIST(GW, MT)                                                                 \
-    return y_dtype == 1                                                                   \
-               ? run(decode_persist_kernel<GW, MT, kLut, true>, persist_waves(MT),       \
-                     persist_blocks_per_cu(GW, MT, kLut))                                  \
-               : run(decode_persist_kernel<GW, MT, kLut, false>, persist_waves(MT),      \
-                     persist_blocks_per_cu(GW, MT, kLut))
-    if constexpr (kLut) {
-      if (m > 16) {
-        QL_PERSIST(2, 2);   // 16 waves: groups per wave <= 2 for K <= 4096
+#define QL_PERSIST(GW, MT)                                                                   \
+    return y_dtype == 1                                                                     \
+               ? run(decode_persist_kernel<GW, MT, kLut, true>, persist_waves(MT, kLut),     \
+                     persist_blocks_per_cu(GW, MT, kLut), persist_lds_bytes(GW, MT, kLut),   \
+                     persist_lds_attr<GW, MT, kLut, true>())                                 \
+               : run(decode_persist_kernel<GW, MT, kLut, false>, persist_waves(MT, kLut),    \
+                     persist_blocks_per_cu(GW, MT, kLut), persist_lds_bytes(GW, MT, kLut),   \
+                     persist_lds_attr<GW, MT, kLut, false>())
+    if (m > 16) {
+      if constexpr (kLut) {
+        QL_PERSIST(2, 2);   // 16 waves: two groups per wave cover K <= 4096
+      } else {
+        if (G <= KW * 2) QL_PERSIST(2, 2);
+        QL_PERSIST(4, 2);
       }
     }
     if (G <= KW * 2) {
