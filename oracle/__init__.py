@@ -20,6 +20,7 @@ Modules
 formats  E2M1 / E4M3 codecs, binary32 and bfloat16 rounding.
 nvfp4    NVFP4 round-to-nearest quantizer (activations and weights).
 int4     Symmetric INT4 quantizer with 128-element groups and bf16 scales.
+sparse24 2:4 magnitude pruning along k on top of int4.
 lut2     2-bit per-row codebook (K-means, Lloyd iterations).
 gemm     Matrix products on dequantized operands and the pass rule.
 
@@ -29,4 +30,4 @@ and special cases (no independent library of K-means is available here):
 "parity unpinned" beyond those invariants.
 """
 
-from . import formats, nvfp4, int4, lut2, gemm  # noqa: F401
+from . import formats, nvfp4, int4, sparse24, lut2, gemm  # noqa: F401

@@ -9,6 +9,8 @@ convention; the pages give no layouts).
 * W4A16 (decode; Disaggregated Quantization: decode switches to a weight-only
   path that leaves activations unquantized; MARLIN article, "どんな技術か":
   FP16 activations times INT4 weights): Y = X W_hat^T with X in bfloat16.
+* W4A16 with 2:4 sparse INT4 weights (MARLIN article, "データの扱い方" and
+  "実験と結果": Sparse-MARLIN): the same product on the pruned weights.
 * LUT2 (decode with a 2-bit codebook; Disaggregated Quantization, full
   disaggregation; KLLM article section 3): Y = X C[idx]^T.
 
@@ -19,7 +21,7 @@ call.
 
 import numpy as np
 
-from . import nvfp4, int4, lut2
+from . import nvfp4, int4, lut2, sparse24
 from .formats import bf16_bits_to_f32
 
 
@@ -32,6 +34,12 @@ def w4a4(a_codes, a_scales, a_st, w_codes, w_scales, w_st):
 def w4a16(x_bf16_bits, w_codes, w_scales):
     x = bf16_bits_to_f32(x_bf16_bits).astype(np.float64)
     return x @ int4.dequantize(w_codes, w_scales).T
+
+
+def w4a16_sp24(x_bf16_bits, w_codes, w_scales):
+    """W4A16 with a 2:4 sparse INT4 blob packed from (w_codes, w_scales): the
+    dense product of the codes the packer keeps (sparse24.keep_codes)."""
+    return w4a16(x_bf16_bits, sparse24.keep_codes(w_codes), w_scales)
 
 
 def lut2_gemm(x_bf16_bits, w_idx, w_centroids):
