@@ -137,7 +137,10 @@ def main():
         c, s = qlin.quantize_int4_g128(f32(synth.weights(dec.cid, li, L.n, L.k)))
         blob = qlin.repack_weights(qlin.QL_INT4_G128, L.n, L.k, c, s)
         x32 = {m: bf16(synth.decode_x_bf16(dec.cid, li, m, L.k)) for m in dec.ms}
-        D.append(dict(L=L, blob=blob, x=x32,
+        c24, s24 = qlin.quantize_int4_g128(f32(synth.weights(dec.cid, li, L.n, L.k)), sparse24=True)
+        blob24 = qlin.repack_weights(qlin.QL_INT4_SP24, L.n, L.k, c24, s24)
+        del c24, s24
+        D.append(dict(L=L, blob=blob, blob24=blob24, x=x32,
                       y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in dec.ms}))
     U = []   # LUT2 decode layers
     for li, L in enumerate(lut.layers):
@@ -228,13 +231,16 @@ def main():
     sweep = {}
     if not args.no_decode_sweep:
         combos = [("w4a16", li, m) for li in range(len(D)) for m in dec.ms] + \
+                 [("w4a16_sp24", li, m) for li in range(len(D)) for m in dec.ms] + \
                  [("lut2", li, m) for li in range(len(U)) for m in lut.ms]
+        fns = {"w4a16": qlin.gemm_w4a16, "w4a16_sp24": qlin.gemm_w4a16_sp24, "lut2": qlin.gemm_lut2}
         for kind, li, m in combos:
-            rec = D[li] if kind == "w4a16" else U[li]
-            fn = qlin.gemm_w4a16 if kind == "w4a16" else qlin.gemm_lut2
+            rec = U[li] if kind == "lut2" else D[li]
+            fn = fns[kind]
+            src = rec["blob24"] if kind == "w4a16_sp24" else rec["blob"]
             L = rec["L"]
-            if m == (dec.ms if kind == "w4a16" else lut.ms)[0]:
-                copies = [rec["blob"].clone() for _ in range(int(np.ceil(600e6 / rec["blob"].numel())))]
+            if m == (lut.ms if kind == "lut2" else dec.ms)[0]:
+                copies = [src.clone() for _ in range(int(np.ceil(600e6 / src.numel())))]
             x, y = rec["x"][m], rec["y"][m]
             for b in copies[:3]:
                 fn(x, b, L.n, L.k, y=y)
@@ -254,14 +260,21 @@ def main():
                 b.synchronize()
                 t.append(a.elapsed_time(b) / len(copies))
             del g
-            wbytes = (L.n * L.k / 2 + L.n * L.k / 64) if kind == "w4a16" else (L.n * L.k / 4 + 8 * L.n)
+            wbytes = {"w4a16": L.n * L.k / 2 + L.n * L.k / 64,
+                      "w4a16_sp24": L.n * L.k / 4 + L.n * L.k / 8 + L.n * L.k / 64,
+                      "lut2": L.n * L.k / 4 + 8 * L.n}[kind]
             by = wbytes + 2.0 * m * L.k + 2.0 * m * L.n
             med, p10, p90 = _pct(t)
             _progress(f"decode {kind}/{L.name}/m{m}: {med * 1e3:.2f} us")
-            sweep[f"{kind}/{L.name}/m{m}"] = {
+            rec_out = {
                 "us": round(med * 1e3, 2), "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2),
                 "gbps": round(by / med / 1e6, 1), "hbm_frac": round(by / med / 1e6 / HBM_GBPS, 3)}
-            if m == (dec.ms if kind == "w4a16" else lut.ms)[-1]:
+            if kind == "w4a16_sp24":
+                dense = sweep.get(f"w4a16/{L.name}/m{m}")
+                if dense:
+                    rec_out["speedup_vs_w4a16"] = round(dense["us"] / (med * 1e3), 3)
+            sweep[f"{kind}/{L.name}/m{m}"] = rec_out
+            if m == (lut.ms if kind == "lut2" else dec.ms)[-1]:
                 del copies
                 torch.cuda.empty_cache()
 
@@ -537,6 +550,7 @@ def main():
             "layers": layers,
             "w4a16_gbps_mean_over_layers": _agg("w4a16", dec.ms),
             "lut2_gbps_mean_over_layers": _agg("lut2", lut.ms),
+            "w4a16_sp24_gbps_mean_over_layers": _agg("w4a16_sp24", dec.ms),
             "decode_sweep": sweep,
             "bf16_reference": bf16_ref,
             "odp_weight_streaming": odp,

@@ -32,6 +32,7 @@ SOURCES = {
     "gemm_w4a4.hip": [],
     "gemm_w4a4_coop.hip": [],
     "gemm_decode.hip": [],
+    "gemm_sparse.hip": [],
 }
 
 COMMON = [

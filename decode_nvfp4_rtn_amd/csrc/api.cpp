@@ -84,7 +84,17 @@ int quantize_int4_g128(const float* w, int64_t n, int64_t k, uint8_t* codes, uin
   if (n == 0 || k == 0) return QL_OK;
   if (!w || !codes || !scales) return QL_EINVAL;
   if (!aligned16(w) || !aligned16(codes)) return QL_EALIGN;
-  return launch_status(launch_quantize_int4(w, n, k, codes, scales, as_stream(stream)));
+  return launch_status(launch_quantize_int4(w, n, k, codes, scales, false, as_stream(stream)));
+}
+
+int quantize_int4_g128_sp24(const float* w, int64_t n, int64_t k, uint8_t* codes,
+                            uint16_t* scales, void* stream) {
+  if (n < 0 || k < 0) return QL_EINVAL;
+  if (k % 128 != 0) return QL_ESHAPE;
+  if (n == 0 || k == 0) return QL_OK;
+  if (!w || !codes || !scales) return QL_EINVAL;
+  if (!aligned16(w) || !aligned16(codes)) return QL_EALIGN;
+  return launch_status(launch_quantize_int4(w, n, k, codes, scales, true, as_stream(stream)));
 }
 
 size_t fit_lut2_workspace(int64_t n, int64_t k) {
@@ -107,14 +117,14 @@ int fit_lut2(const float* w, int64_t n, int64_t k, uint8_t* idx, uint16_t* centr
 }
 
 size_t repack_weights_bytes(int fmt, int64_t n, int64_t k) {
-  if (fmt < QL_NVFP4 || fmt > QL_LUT2 || n <= 0 || k <= 0) return 0;
+  if (fmt < QL_NVFP4 || fmt > QL_INT4_SP24 || n <= 0 || k <= 0) return 0;
   return blob_layout(fmt, n, k).total;
 }
 
 int repack_weights(int fmt, int64_t n, int64_t k, const uint8_t* codes,
                    const void* scales_or_lut, const float* tensor_scale, void* packed,
                    size_t packed_bytes, void* stream) {
-  if (fmt < QL_NVFP4 || fmt > QL_LUT2) return QL_EFORMAT;
+  if (fmt < QL_NVFP4 || fmt > QL_INT4_SP24) return QL_EFORMAT;
   if (n < 0 || k < 0) return QL_EINVAL;
   if (n % 16 != 0 || k % 128 != 0) return QL_ESHAPE;
   if (n > (int64_t(1) << 24) || k > (int64_t(1) << 20)) return QL_ESHAPE;
@@ -156,6 +166,16 @@ int gemm_lut2(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, in
   if (!aligned16(x_bf16)) return QL_EALIGN;
   return launch_status(launch_gemm_lut2(x_bf16, w_packed, m, n, k, y, y_dtype,
                                         as_stream(stream)));
+}
+
+int gemm_w4a16_sp24(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, int64_t k,
+                    void* y, int y_dtype, void* stream) {
+  int st = check_gemm(w_packed, y, m, n, k, y_dtype);
+  if (st >= 0) return st;
+  if (!x_bf16) return QL_EINVAL;
+  if (!aligned16(x_bf16)) return QL_EALIGN;
+  return launch_status(launch_gemm_w4a16_sp24(x_bf16, w_packed, m, n, k, y, y_dtype,
+                                              as_stream(stream)));
 }
 
 }  // extern "C"

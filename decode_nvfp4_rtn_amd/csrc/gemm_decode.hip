@@ -33,42 +33,10 @@
 //   ワープの配置") and their partial sums are added in LDS in a fixed order,
 //   so results are deterministic and no atomics are used.
 #include "qlin_internal.hpp"
+#include "decode_ops.hpp"
 
 namespace qlin {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int KW = 8;  // wavefronts per block (k split)
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// A 32-bit constant held in a VGPR, so that two-constant operations such as
-// (w & mask) | bias can use one v_and_or_b32 (VOP3 on this target accepts no
-// literal constants and one scalar operand).
-__device__ __forceinline__ uint32_t vconst(uint32_t c) {
-  uint32_t v;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
-  return v;
-}
-
-// INT4: dword of 8 nibbles (pairs at bits (4j, 16+4j)) -> bf16 (128+u) x 8
-__device__ __forceinline__ bf16x8_t int4_operand(uint32_t w, uint32_t mask, uint32_t bias) {
-  u32x4 v;
-  v[0] = (w & mask) | bias;
-  v[1] = ((w >> 4) & mask) | bias;
-  v[2] = ((w >> 8) & mask) | bias;
-  v[3] = ((w >> 12) & mask) | bias;
-  return as_bf16x8(v);
-}
 
 // LUT2: 16 2-bit indices (layout of the repacked blob) -> two bf16x8 operands
 // (sub-steps 2d and 2d+1) looked up in the row's codebook with v_perm_b32.
@@ -496,11 +464,6 @@ constexpr size_t persist_lds_bytes(int gw, int mt, bool lut) {
          (persist_x_in_lds(mt, lut) ? size_t(persist_waves(mt, lut)) * gw * 4 * 64 * 16 : 0);
 }
 
-// Buffer resource word 3 for raw 32-bit buffer loads, and the non-temporal
-// cache policy for streamed weights.
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kPolicyNT = 2;
-
 template <int GW, int MT, bool kLut, bool kBF16Out>
 __global__ __launch_bounds__(persist_waves(MT, kLut) * 64,
                              persist_waves(MT, kLut) / 4 * persist_blocks_per_cu(GW, MT, kLut))
@@ -741,23 +704,6 @@ constexpr int chunk_cap(bool lut, int mt, int ntb, int kwt) {
                    : (lut ? 16 : (mt * ntb == 1 ? 16 : (mt * ntb == 2 ? 8 : 2)));
 }
 
-constexpr int cmin(int a, int b) { return a < b ? a : b; }
-
-// Chunk of groups whose weight loads a wave issues at once.  Loads in flight
-// hide HBM latency; a chunk boundary costs roughly one extra round trip and a
-// padded slot one wasted load, so pick the size that minimises the sum.
-int pick_chunk(int gpw, int cap) {
-  static const int kSizes[] = {2, 4, 6, 8, 12, 16};
-  int best = 2, best_cost = 1 << 30;
-  for (int w : kSizes) {
-    if (w > cap) break;
-    const int chunks = (gpw + w - 1) / w;
-    const int cost = chunks * w + 2 * chunks;
-    if (cost < best_cost) best = w, best_cost = cost;
-  }
-  return best;
-}
-
 template <bool kLut, int MT, int NTB, int KWT>
 hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout& L, int M,
                            int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
@@ -772,19 +718,6 @@ hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout&
     case 12: return launch_decode<kLut, MT, NTB, cmin(12, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
     default: return launch_decode<kLut, MT, NTB, cmin(16, kCap), KWT>(x, blob, L, M, m0, N, K, y, y_dtype, s);
   }
-}
-
-// Compute units of the current device (cached per device; 0 if unknown).
-int device_cu_count() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = v;
-  }
-  return cache[dev];
 }
 
 template <bool kLut>

@@ -44,7 +44,8 @@ static_assert(sizeof(BlobHeader) == 256, "header size");
 // and the GEMM launchers.
 struct BlobLayout {
   size_t codes_off, codes_bytes;
-  size_t aux_off, aux_bytes;  // scales or codebook
+  size_t aux_off, aux_bytes;    // scales or codebook
+  size_t meta_off, meta_bytes;  // 2:4 sparse INT4 only: kept positions (else 0)
   size_t total;
 };
 
@@ -59,11 +60,20 @@ inline BlobLayout blob_layout(int fmt, int64_t n, int64_t k) {
   } else if (fmt == 1) {   // INT4 g128: codes n*k/2, bf16 scales n*k/128*2
     L.codes_bytes = size_t(n) * k / 2;
     L.aux_bytes = size_t(n) * (k / 128) * 2;
+  } else if (fmt == 3) {   // 2:4 INT4 g128: kept codes n*k/4, positions n*k/8, scales
+    L.codes_bytes = size_t(n) * k / 4;
+    L.meta_bytes = size_t(n) * k / 8;
+    L.aux_bytes = size_t(n) * (k / 128) * 2;
   } else {                 // LUT2: indices n*k/4, codebook 8 bytes per row
     L.codes_bytes = size_t(n) * k / 4;
     L.aux_bytes = size_t(n) * 8;
   }
-  L.aux_off = align256(L.codes_off + L.codes_bytes);
+  size_t end = L.codes_off + L.codes_bytes;
+  if (L.meta_bytes) {
+    L.meta_off = align256(end);
+    end = L.meta_off + L.meta_bytes;
+  }
+  L.aux_off = align256(end);
   L.total = align256(L.aux_off + L.aux_bytes);
   return L;
 }
@@ -78,7 +88,7 @@ hipError_t launch_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64
                                  bool static_scale, uint32_t* partial, hipStream_t s);
 
 hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* codes,
-                                uint16_t* scales, hipStream_t s);
+                                uint16_t* scales, bool prune24, hipStream_t s);
 size_t lut2_workspace(int64_t n, int64_t k);
 hipError_t launch_fit_lut2(const float* w, int64_t n, int64_t k, uint8_t* idx,
                            uint16_t* centroids, void* ws, hipStream_t s);
@@ -95,6 +105,8 @@ hipError_t launch_gemm_w4a4_coop(const uint8_t* a_codes, const uint8_t* a_scales
                                  int64_t k, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n,
                              int64_t k, void* y, int y_dtype, hipStream_t s);
+hipError_t launch_gemm_w4a16_sp24(const void* x, const void* w_packed, int64_t m, int64_t n,
+                                  int64_t k, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm_lut2(const void* x, const void* w_packed, int64_t m, int64_t n,
                             int64_t k, void* y, int y_dtype, hipStream_t s);
 

@@ -20,6 +20,18 @@
 //          4j and t = 2j+1 at bits 16+4j (so OR-ing 0x4300 into each 16-bit
 //          half yields the bf16 value 128 + u of two neighbours at once)
 //   scales [nt][ks][16 rows] bf16
+// 2:4 sparse INT4 group-128 (Sparse-MARLIN reading, W4A16 decode on the
+// gfx950 2:4 sparse MFMA v_smfmac_f32_16x16x64_bf16):
+//   codes  [nt][ks][64 lanes][8 B]  dword s (0, 1) covers k = 128 ks + 64 s +
+//          16 (2 (q % 2) + h) + 8 (q / 2) + 4 b + p for quads g = 2 h + b
+//          (h, b in {0, 1}) and p = 0..3; element 2g holds the code at the
+//          lower kept position p0 of quad g, element 2g+1 the one at p1, with
+//          element e at bits 4 (e/2) (e even) or 16 + 4 (e/2) (e odd)
+//   meta   [nt][ks][64 lanes][4 B]  the kept positions: p of element e of
+//          dword s at bits 16 s + 2 e (the sparse MFMA's index operand)
+//   scales [nt][ks][16 rows] bf16
+//   Kept per quad: the two codes of largest |q| (ties to the lower column),
+//   i.e. every nonzero code when the codes come from the 2:4 quantizer.
 // LUT2 (2-bit codebook decode):
 //   codes  [nt][ks][64 lanes][8 B]  dword d holds sub-steps s = 2d, 2d+1;
 //          index of (s, t) at bit 8 (t % 4) + 2 (2 (s % 2) + t / 4), so that
@@ -155,6 +167,47 @@ __global__ void repack_lut2_book(const uint16_t* __restrict__ cent, int64_t n,
   }
 }
 
+// 2:4 INT4: one thread per (lane, 128-k step) writes its 8 code bytes and
+// its 4 position bytes.
+__global__ void repack_sp24(const uint8_t* __restrict__ codes, int64_t n, int64_t k,
+                            uint2* __restrict__ out_codes, uint32_t* __restrict__ out_meta) {
+  const int64_t units = n * k / 32;
+  const int64_t KT = k / 128;
+  for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units;
+       u += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t l = u % 64, tile = u / 64;
+    const int64_t nt = tile / KT, ks = tile % KT;
+    const int64_t row = nt * 16 + (l % 16), qa = l / 16;
+    uint32_t cw[2] = {0u, 0u}, meta = 0u;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t kb = ks * 128 + 64 * s + 16 * (2 * (qa & 1) + (g >> 1)) + 8 * (qa >> 1) +
+                           4 * (g & 1);
+        const uint8_t* src = codes + row * (k / 2) + kb / 2;
+        const uint32_t uq[4] = {uint32_t(src[0] & 15u), uint32_t(src[0] >> 4),
+                                uint32_t(src[1] & 15u), uint32_t(src[1] >> 4)};
+        int pos[2] = {0, 1}, nk = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int ac = int(uq[c]) - 8 < 0 ? 8 - int(uq[c]) : int(uq[c]) - 8;
+          int beaten = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ae = int(uq[e]) - 8 < 0 ? 8 - int(uq[e]) : int(uq[e]) - 8;
+            beaten += (ae > ac || (ae == ac && e < c)) ? 1 : 0;
+          }
+          if (beaten < 2 && nk < 2) pos[nk++] = c;
+        }
+        cw[s] |= (uq[pos[0]] << (4 * g)) | (uq[pos[1]] << (16 + 4 * g));
+        meta |= (uint32_t(pos[0]) << (16 * s + 4 * g)) | (uint32_t(pos[1]) << (16 * s + 4 * g + 2));
+      }
+    out_codes[u] = make_uint2(cw[0], cw[1]);
+    out_meta[u] = meta;
+  }
+}
+
 int grid_for(int64_t units) {
   int64_t b = (units + 255) / 256;
   if (b > 65536) b = 65536;
@@ -172,9 +225,14 @@ hipError_t launch_repack(int fmt, int64_t n, int64_t k, const uint8_t* codes, co
     repack_nvfp4_codes<<<grid_for(n * k / 32), 256, 0, s>>>(codes, n, k, base + L.codes_off);
     repack_nvfp4_scales<<<grid_for(n * k / 128), 256, 0, s>>>(
         static_cast<const uint8_t*>(aux), n, k, base + L.aux_off);
-  } else if (fmt == 1) {
-    repack_int4_codes<<<grid_for(n * k / 8), 256, 0, s>>>(
-        codes, n, k, reinterpret_cast<uint32_t*>(base + L.codes_off));
+  } else if (fmt == 1 || fmt == 3) {
+    if (fmt == 1)
+      repack_int4_codes<<<grid_for(n * k / 8), 256, 0, s>>>(
+          codes, n, k, reinterpret_cast<uint32_t*>(base + L.codes_off));
+    else
+      repack_sp24<<<grid_for(n * k / 32), 256, 0, s>>>(
+          codes, n, k, reinterpret_cast<uint2*>(base + L.codes_off),
+          reinterpret_cast<uint32_t*>(base + L.meta_off));
     repack_int4_scales<<<grid_for(n * (k / 128)), 256, 0, s>>>(
         static_cast<const uint16_t*>(aux), n, k, reinterpret_cast<uint16_t*>(base + L.aux_off));
   } else {

@@ -28,15 +28,39 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// kPrune: 2:4 magnitude pruning first (MARLIN article, "データの扱い方":
+// Sparse-MARLIN's 2:4 structured sparsity).  Of every four consecutive
+// columns the two of largest |w| are kept (ties to the lower column) and the
+// other two become zero before the group is quantized; a quad spans lanes
+// 2j and 2j+1, which swap their pair of values to rank all four.
+template <bool kPrune>
 __global__ __launch_bounds__(256) void int4_kernel(const float* __restrict__ w, int64_t n,
                                                    int64_t k, uint8_t* __restrict__ codes,
                                                    uint16_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int64_t G = k / 128;
   const int64_t grp = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (grp >= n * G) return;
+  if (grp >= n * G) return;   // wave-uniform: whole wavefronts exit together
   const int64_t row = grp / G, g = grp % G;
-  const float2 v = reinterpret_cast<const float2*>(w + row * k + g * 128)[lane];
+  float2 v = reinterpret_cast<const float2*>(w + row * k + g * 128)[lane];
+  if (kPrune) {
+    const float o0 = __shfl_xor(v.x, 1, 64), o1 = __shfl_xor(v.y, 1, 64);
+    // quad columns 0..3: this lane holds 2 (lane & 1) and 2 (lane & 1) + 1
+    const int c0 = 2 * (lane & 1);
+    const float q[4] = {(lane & 1) ? o0 : v.x, (lane & 1) ? o1 : v.y,
+                        (lane & 1) ? v.x : o0, (lane & 1) ? v.y : o1};
+    auto kept = [&](int c) {
+      int beaten = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ae = __builtin_fabsf(q[e]), ac = __builtin_fabsf(q[c]);
+        beaten += (ae > ac || (ae == ac && e < c)) ? 1 : 0;
+      }
+      return beaten < 2;
+    };
+    if (!kept(c0)) v.x = 0.0f;
+    if (!kept(c0 + 1)) v.y = 0.0f;
+  }
   float a = __builtin_fmaxf(__builtin_fabsf(v.x), __builtin_fabsf(v.y));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off, 64));
@@ -175,10 +199,13 @@ __global__ __launch_bounds__(256) void lut2_assign_kernel(const float* __restric
 }  // namespace
 
 hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* codes,
-                                uint16_t* scales, hipStream_t s) {
+                                uint16_t* scales, bool prune24, hipStream_t s) {
   const int64_t groups = n * (k / 128);
   const int64_t blocks = (groups + 3) / 4;
-  int4_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(w, n, k, codes, scales);
+  if (prune24)
+    int4_kernel<true><<<static_cast<unsigned>(blocks), 256, 0, s>>>(w, n, k, codes, scales);
+  else
+    int4_kernel<false><<<static_cast<unsigned>(blocks), 256, 0, s>>>(w, n, k, codes, scales);
   return hipGetLastError();
 }
 

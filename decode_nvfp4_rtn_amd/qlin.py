@@ -24,7 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 QL_OK, QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EDTYPE, QL_EWORKSPACE, QL_EHIP, QL_EFORMAT = range(8)
 QL_F32, QL_BF16 = 0, 1
-QL_NVFP4, QL_INT4_G128, QL_LUT2 = 0, 1, 2
+QL_NVFP4, QL_INT4_G128, QL_LUT2, QL_INT4_SP24 = 0, 1, 2, 3
 QL_STATIC_SCALE = 1
 
 _vp, _i64, _sz, _int, _uint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
@@ -35,6 +35,7 @@ _SIGS = {
     "quantize_nvfp4_workspace": (_sz, [_i64, _i64]),
     "quantize_nvfp4": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _uint, _vp, _sz, _vp]),
     "quantize_int4_g128": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "quantize_int4_g128_sp24": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "fit_lut2_workspace": (_sz, [_i64, _i64]),
     "fit_lut2": (_int, [_vp, _i64, _i64, _vp, _vp, _vp, _sz, _vp]),
     "repack_weights_bytes": (_sz, [_int, _i64, _i64]),
@@ -42,6 +43,7 @@ _SIGS = {
     "gemm_w4a4": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "gemm_w4a16": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "gemm_lut2": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "gemm_w4a16_sp24": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -123,8 +125,9 @@ def quantize_nvfp4(x, tensor_scale=None, codes=None, scales=None, workspace=None
     return codes, scales, ts
 
 
-def quantize_int4_g128(w, codes=None, scales=None, stream=None):
-    """Symmetric INT4 group-128 quantization of fp32 weights [n, k].
+def quantize_int4_g128(w, codes=None, scales=None, stream=None, sparse24=False):
+    """Symmetric INT4 group-128 quantization of fp32 weights [n, k]; with
+    sparse24, 2:4 magnitude pruning along k first (quantize_int4_g128_sp24).
     Returns (codes uint8 [n, k/2], scales int16 (bf16 bits) [n, k/128])."""
     _dev(w, "w")
     n, k = w.shape
@@ -132,8 +135,8 @@ def quantize_int4_g128(w, codes=None, scales=None, stream=None):
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
     if scales is None:
         scales = torch.empty((n, k // 128), dtype=torch.int16, device=w.device)
-    _check("quantize_int4_g128", _lib.quantize_int4_g128(
-        _ptr(w), n, k, _ptr(codes), _ptr(scales), _stream(stream)))
+    name = "quantize_int4_g128_sp24" if sparse24 else "quantize_int4_g128"
+    _check(name, getattr(_lib, name)(_ptr(w), n, k, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
 
@@ -210,6 +213,16 @@ def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
     y, dt = _out(y, m, n, out_dtype, x.device)
     _check("gemm_lut2", _lib.gemm_lut2(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
                                        _stream(stream)))
+    return y
+
+
+def gemm_w4a16_sp24(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
+    """2:4 sparse W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times 2:4 INT4 weights^T."""
+    _dev(x, "x")
+    m = x.shape[0]
+    y, dt = _out(y, m, n, out_dtype, x.device)
+    _check("gemm_w4a16_sp24", _lib.gemm_w4a16_sp24(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
+                                                   _stream(stream)))
     return y
 
 

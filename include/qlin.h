@@ -58,7 +58,7 @@ typedef enum {
 } ql_status;
 
 typedef enum { QL_F32 = 0, QL_BF16 = 1 } ql_dtype;
-typedef enum { QL_NVFP4 = 0, QL_INT4_G128 = 1, QL_LUT2 = 2 } ql_format;
+typedef enum { QL_NVFP4 = 0, QL_INT4_G128 = 1, QL_LUT2 = 2, QL_INT4_SP24 = 3 } ql_format;
 
 /* quantize_nvfp4 flag: read *tensor_scale as the (calibrated) tensor scale
  * instead of computing it from the tensor's absolute maximum. */
@@ -113,6 +113,21 @@ int quantize_int4_g128(const float *w, int64_t n, int64_t k, uint8_t *codes,
                        uint16_t *scales, void *stream);
 
 /* ------------------------------------------------------------------------
+ * 2:4 structured-sparse INT4 group-128 quantization (MARLIN article,
+ * "データの扱い方" and "実験と結果": Sparse-MARLIN combines the group-128
+ * INT4 format with 2:4 structured sparsity).  The pages do not say how the
+ * pattern is chosen; here: in every run of four consecutive columns of a row
+ * the two entries of largest |w| are kept (ties to the lower column) and the
+ * other two are set to zero, then the row is quantized exactly as by
+ * quantize_int4_g128 (so pruned entries have q = 0, u = 8).
+ *
+ * Arguments, outputs, shapes and errors as quantize_int4_g128; the codes are
+ * in the same dense canonical layout, with at most two nonzero q per quad.
+ * ---------------------------------------------------------------------- */
+int quantize_int4_g128_sp24(const float *w, int64_t n, int64_t k, uint8_t *codes,
+                            uint16_t *scales, void *stream);
+
+/* ------------------------------------------------------------------------
  * 2-bit codebook (LUT2) fit: per weight row, 4 centroids by 10 Lloyd
  * K-means iterations (KLLM article, aibr.jp, sections 1 and 3: K-means
  * quantization into centroids plus an index matrix; Disaggregated
@@ -140,10 +155,15 @@ int fit_lut2(const float *w, int64_t n, int64_t k, uint8_t *idx,
  * operand order read by the GEMM kernels (an opaque, versioned blob with a
  * header).  Pure data movement: values are not changed.
  *
- * fmt            QL_NVFP4 | QL_INT4_G128 | QL_LUT2.
+ * fmt            QL_NVFP4 | QL_INT4_G128 | QL_LUT2 | QL_INT4_SP24.
  * codes          canonical codes as produced by quantize_nvfp4 (NVFP4, from
- *                W [n,k]), quantize_int4_g128 or fit_lut2.
- * scales_or_lut  E4M3 [n, k/16] | bf16 [n, k/128] | bf16 centroids [n, 4].
+ *                W [n,k]), quantize_int4_g128 / quantize_int4_g128_sp24, or
+ *                fit_lut2.  QL_INT4_SP24 keeps, in each run of four
+ *                consecutive columns, the two codes of largest |q| (ties to
+ *                the lower column) with their positions: every nonzero code
+ *                when the codes come from quantize_int4_g128_sp24.
+ * scales_or_lut  E4M3 [n, k/16] | bf16 [n, k/128] (INT4 and INT4_SP24) |
+ *                bf16 centroids [n, 4].
  * tensor_scale   device fp32 s_t of the weights (NVFP4 only, else NULL);
  *                copied into the blob.
  * packed         out, >= repack_weights_bytes(fmt, n, k) bytes.
@@ -196,6 +216,18 @@ int gemm_w4a16(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
  * ---------------------------------------------------------------------- */
 int gemm_lut2(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
               int64_t k, void *y, int y_dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * 2:4 sparse W4A16 decode GEMV / skinny GEMM (MARLIN article, "実験と結果":
+ * Sparse-MARLIN), on gfx950's 2:4 sparse MFMA:
+ *   Y[m,n] = sum_g s[n,g] sum_{k in g, kept} x[m,k] q[n,k]   (fp32 accumulation)
+ * x        [m, k] bf16.   w_packed: QL_INT4_SP24 blob from repack_weights.
+ * y        out [m, n], QL_F32 or QL_BF16.
+ * Tuned for m <= 32; any m >= 0 is accepted.
+ * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
+ * ---------------------------------------------------------------------- */
+int gemm_w4a16_sp24(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
+                    int64_t k, void *y, int y_dtype, void *stream);
 
 #ifdef __cplusplus
 }

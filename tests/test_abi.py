@@ -33,6 +33,7 @@ def lib():
         "quantize_nvfp4_workspace": (sz, [i64, i64]),
         "quantize_nvfp4": (i, [vp, i, i64, i64, vp, vp, vp, u, vp, sz, vp]),
         "quantize_int4_g128": (i, [vp, i64, i64, vp, vp, vp]),
+        "quantize_int4_g128_sp24": (i, [vp, i64, i64, vp, vp, vp]),
         "fit_lut2_workspace": (sz, [i64, i64]),
         "fit_lut2": (i, [vp, i64, i64, vp, vp, vp, sz, vp]),
         "repack_weights_bytes": (sz, [i, i64, i64]),
@@ -40,6 +41,7 @@ def lib():
         "gemm_w4a4": (i, [vp, vp, vp, vp, i64, i64, i64, vp, i, vp]),
         "gemm_w4a16": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
         "gemm_lut2": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
+        "gemm_w4a16_sp24": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -53,7 +55,8 @@ B, C, D, E = 0x20000, 0x30000, 0x40000, 0x50000
 
 def test_header_declares_the_boundary():
     names = set(_declared())
-    for n in ("quantize_nvfp4", "repack_weights", "gemm_w4a4", "gemm_w4a16", "gemm_lut2"):
+    for n in ("quantize_nvfp4", "repack_weights", "gemm_w4a4", "gemm_w4a16", "gemm_lut2",
+              "quantize_int4_g128_sp24", "gemm_w4a16_sp24"):
         assert n in names
 
 
@@ -88,6 +91,9 @@ def test_weight_prep_validation(lib):
     assert lib.quantize_int4_g128(A, 16, 100, B, C, None) == QL_ESHAPE
     assert lib.quantize_int4_g128(None, 16, 128, B, C, None) == QL_EINVAL
     assert lib.quantize_int4_g128(None, 0, 128, None, None, None) == QL_OK
+    assert lib.quantize_int4_g128_sp24(A, 16, 100, B, C, None) == QL_ESHAPE
+    assert lib.quantize_int4_g128_sp24(A, 16, 128, B + 4, C, None) == QL_EALIGN
+    assert lib.quantize_int4_g128_sp24(None, 0, 128, None, None, None) == QL_OK
     assert lib.fit_lut2(A, 16, 33024, B, C, D, 1 << 20, None) == QL_ESHAPE
     assert lib.fit_lut2(A, 16, 128, B, C, D, 0, None) == QL_EWORKSPACE
     assert lib.fit_lut2(A, 16, 128, B + 2, C, D, 1 << 20, None) == QL_EALIGN
@@ -100,15 +106,15 @@ def test_repack_validation_and_sizes(lib):
     assert r(0, 16, 120, A, B, C, D, 1 << 20, None) == QL_ESHAPE
     assert r(0, 16, 128, A, B, None, D, 1 << 20, None) == QL_EINVAL   # NVFP4 needs s_t
     assert r(1, 16, 128, A, B, None, D, 10, None) == QL_EWORKSPACE
-    for fmt, per in ((0, 0.5 + 1 / 16), (1, 0.5 + 2 / 128), (2, 0.25)):
+    for fmt, per in ((0, 0.5 + 1 / 16), (1, 0.5 + 2 / 128), (2, 0.25), (3, 0.25 + 0.125 + 2 / 128)):
         for n, k in ((16, 128), (4096, 4096), (30720, 3840)):
             nb = lib.repack_weights_bytes(fmt, n, k)
             assert nb % 256 == 0 and nb >= 256 + n * k * per
-            assert nb <= 256 + n * k * per + 2 * 256 + (8 * n if fmt == 2 else 0)
+            assert nb <= 256 + n * k * per + 3 * 256 + (8 * n if fmt == 2 else 0)
     assert lib.repack_weights_bytes(5, 16, 128) == 0
 
 
-@pytest.mark.parametrize("fn", ["gemm_w4a16", "gemm_lut2"])
+@pytest.mark.parametrize("fn", ["gemm_w4a16", "gemm_lut2", "gemm_w4a16_sp24"])
 def test_decode_gemm_validation(lib, fn):
     g = getattr(lib, fn)
     assert g(A, B, 1, 20, 128, C, 1, None) == QL_ESHAPE
