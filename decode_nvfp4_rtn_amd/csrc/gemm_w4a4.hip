@@ -271,7 +271,11 @@ hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, con
   // double buffer is 160 KiB), so it needs at least one tile per CU; smaller
   // problems take the 128x128 per-wave kernel, which spreads 4x more blocks.
   const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (big_tiles >= 256)
+  // the block-cooperative kernel addresses activation and weight codes with
+  // 31-bit buffer offsets
+  const int64_t lim = (int64_t(1) << 31) - (int64_t(1) << 20);
+  const bool offsets_fit = m * (k / 2) <= lim && n * (k / 2) <= lim;
+  if (big_tiles >= 256 && offsets_fit)
     return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype, s);
   return launch_tile<4, 4>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
 }

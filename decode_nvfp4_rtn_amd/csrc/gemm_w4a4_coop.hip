@@ -57,15 +57,13 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, half2_t s) {
                __builtin_bit_cast(uint32_t, cvt2(w, 3) * s)};
 }
 
+// E4M3 scale g (0..3) of a dword of four, as an fp16 pair: one packed
+// conversion per two scales (exact: every E4M3 value is an fp16 value; an
+// exhaustive GPU check of all byte pairs agreed), broadcast by the multiply
 __device__ __forceinline__ half2_t scale_h2(uint32_t w4, int g) {
-  float f;
-  switch (g) {
-    case 0: f = __builtin_amdgcn_cvt_f32_fp8(w4, 0); break;
-    case 1: f = __builtin_amdgcn_cvt_f32_fp8(w4, 1); break;
-    case 2: f = __builtin_amdgcn_cvt_f32_fp8(w4, 2); break;
-    default: f = __builtin_amdgcn_cvt_f32_fp8(w4, 3); break;
-  }
-  const _Float16 h = static_cast<_Float16>(f);
+  const half2_t two = g < 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w4, 1.0f, false)
+                            : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w4, 1.0f, true);
+  const _Float16 h = two[g & 1];
   return half2_t{h, h};
 }
 
@@ -113,29 +111,41 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   const int NT16 = N / 16;
 
   // dequantization rows of this thread: row j of 512 = tid + j * NTHR; rows < 256
-  // are weight rows n0 + row, the rest activation rows m0 + row - 256.  Rows
-  // past N or M are clamped to the last valid one: their products only reach
-  // outputs that are never stored, and the loads stay unconditional (a load
-  // under a branch makes the compiler wait for every outstanding load where
-  // the branch rejoins, which would expose the prefetch latency each stage).
-  const uint8_t* src[ROWS];
-  const uint8_t* ssrc[ROWS];
+  // are weight rows n0 + row, the rest activation rows m0 + row - 256 (the same
+  // kind for a whole wavefront).  Rows past N or M are clamped to the last
+  // valid one: their products only reach outputs that are never stored, and
+  // the loads stay unconditional (a load under a branch makes the compiler
+  // wait for every outstanding load where the branch rejoins, which would
+  // expose the prefetch latency each stage).  Loads go through buffer
+  // resources: the row offset is a per-thread constant, the stage offset
+  // and the operand are wave-uniform, so no vector instruction computes an
+  // address (offsets fit 31 bits; the launcher checks).
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t rcw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(blob + wc_off), 0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(blob + ws_off), 0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rcx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(xcodes), 0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(xscales), 0, 0x7FFFFFFF, 0x00020000);
   bool isw[ROWS];
   int lrow[ROWS];
+  uint32_t vc[ROWS], vs[ROWS];
 #pragma unroll
   for (int j = 0; j < ROWS; ++j) {
     const int row = tid + j * NTHR;
-    isw[j] = row < 256;
+    isw[j] = wave_u * 64 + j * NTHR < 256;   // wave-uniform
     lrow[j] = row & 255;
     if (isw[j]) {
       const int wrow = n0 + row;
-      const int64_t wt = min(wrow >> 4, NT16 - 1);
-      src[j] = blob + wc_off + (wt * KT * 16 + (wrow & 15)) * 64;
-      ssrc[j] = blob + ws_off + (wt * KT * 16 + (wrow & 15)) * 8;
+      const uint32_t wt = uint32_t(min(wrow >> 4, NT16 - 1));
+      vc[j] = (wt * uint32_t(KT) * 16u + uint32_t(wrow & 15)) * 64u;
+      vs[j] = (wt * uint32_t(KT) * 16u + uint32_t(wrow & 15)) * 8u;
     } else {
-      const int64_t xrow = min(m0 + row - 256, M - 1);
-      src[j] = xcodes + xrow * (K / 2);
-      ssrc[j] = xscales + xrow * (K / 16);
+      const uint32_t xrow = uint32_t(min(m0 + row - 256, M - 1));
+      vc[j] = xrow * uint32_t(K / 2);
+      vs[j] = xrow * uint32_t(K / 16);
     }
   }
 
@@ -149,18 +159,14 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   auto gload = [&](Regs& R, int st) {
 #pragma unroll
     for (int j = 0; j < ROWS; ++j) {
-      int64_t coff, soff;
-      if (isw[j]) {
-        coff = int64_t(st >> 1) * 16 * 64 + (st & 1) * 32;
-        soff = int64_t(st >> 1) * 16 * 8 + (st & 1) * 4;
-      } else {
-        coff = int64_t(st) * 32;
-        soff = int64_t(st) * 4;
-      }
-      const uint4* p = reinterpret_cast<const uint4*>(src[j] + coff);
-      R.c[j][0] = p[0];
-      R.c[j][1] = p[1];
-      R.sc[j] = *reinterpret_cast<const uint32_t*>(ssrc[j] + soff);
+      const int co = isw[j] ? (st >> 1) * 1024 + (st & 1) * 32 : st * 32;
+      const int so = isw[j] ? (st >> 1) * 128 + (st & 1) * 4 : st * 4;
+      const __amdgpu_buffer_rsrc_t rc = isw[j] ? rcw : rcx, rs = isw[j] ? rsw : rsx;
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rc, vc[j], co, 0);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rc, vc[j], co + 16, 0);
+      R.c[j][0] = make_uint4(a[0], a[1], a[2], a[3]);
+      R.c[j][1] = make_uint4(b[0], b[1], b[2], b[3]);
+      R.sc[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, vs[j], so, 0);
     }
   };
   // dequantize dword e (0 .. DW-1) of this thread's rows into LDS buffer buf
