@@ -132,6 +132,8 @@ def main():
                       ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(M, L.k)),
                                      dtype=torch.uint8, device=dev),
                       y=torch.empty((M, L.n), dtype=torch.bfloat16, device=dev)))
+        gb = qlin.gemm_w4a4_workspace(M, L.n, L.k)   # 0 when the tiles fill whole rounds
+        P[-1]["gws"] = torch.empty(gb, dtype=torch.uint8, device=dev) if gb else None
     D = []   # W4A16 decode layers
     for li, L in enumerate(dec.layers):
         c, s = qlin.quantize_int4_g128(f32(synth.weights(dec.cid, li, L.n, L.k)))
@@ -168,7 +170,8 @@ def main():
                                 workspace=p["ws"], ts_out=p["ts"])
             if ev is not None:
                 ev[i][1].record()
-            qlin.gemm_w4a4(p["codes"], p["scales"], p["ts"], p["blob"], M, L.n, L.k, y=p["y"])
+            qlin.gemm_w4a4(p["codes"], p["scales"], p["ts"], p["blob"], M, L.n, L.k, y=p["y"],
+                           workspace=p["gws"])
             if ev is not None:
                 ev[i][2].record()
         if ev is not None:
@@ -391,6 +394,10 @@ def main():
                           ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(MB, L.k)),
                                          dtype=torch.uint8, device=dev),
                           y=torch.empty((MB, L.n), dtype=torch.bfloat16, device=dev)))
+            # k split of a partly filled last round of tiles (fp32 partials)
+            R[-1]["gws_bytes"] = {m: qlin.gemm_w4a4_workspace(m, L.n, L.k) for m in b27.ms}
+            nb = max(R[-1]["gws_bytes"].values())
+            R[-1]["gws"] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         torch.cuda.synchronize()
         _progress("27B-class inputs and packed weights resident")
         reps = 5
@@ -406,7 +413,8 @@ def main():
                                         workspace=r["ws"], ts_out=r["ts"])
                     e1.record()
                     qlin.gemm_w4a4(r["codes"][:m], r["scales"][:m], r["ts"], r["blob"], m, L.n, L.k,
-                                   y=r["y"][:m])
+                                   y=r["y"][:m],
+                                   workspace=r["gws"] if r["gws_bytes"][m] else None)
                     e2.record()
                     if rep > 0:   # the first round is a warm-up
                         tq[(m, i)].append((e0, e1))
@@ -421,7 +429,8 @@ def main():
                 fl = 2.0 * m * L.n * L.k
                 fl_all, q_all, g_all = fl_all + fl, q_all + q, g_all + g
                 rows.append({"layer": L.name, "n": L.n, "k": L.k, "gemm_us": round(g * 1e3, 1),
-                             "gemm_tflops": round(fl / g / 1e9, 1), "quantize_us": round(q * 1e3, 1)})
+                             "gemm_tflops": round(fl / g / 1e9, 1), "quantize_us": round(q * 1e3, 1),
+                             "k_split_workspace_mb": round(r["gws_bytes"][m] / 1e6, 1)})
             big[f"m{m}"] = {
                 "layers": rows,
                 "gemm_tflops": round(fl_all / g_all / 1e9, 1),

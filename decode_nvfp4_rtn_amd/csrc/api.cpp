@@ -145,7 +145,29 @@ int gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_te
   if (!a_codes || !a_scales || !a_tensor_scale) return QL_EINVAL;
   if (!aligned16(a_codes) || !aligned16(a_scales)) return QL_EALIGN;
   return launch_status(launch_gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k,
-                                        y, y_dtype, as_stream(stream)));
+                                        y, y_dtype, nullptr, 0, as_stream(stream)));
+}
+
+size_t gemm_w4a4_workspace(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || n % 16 != 0 || k % 128 != 0) return 0;
+  if (m > (int64_t(1) << 31) / 2 || n > (int64_t(1) << 24) || k > (int64_t(1) << 20)) return 0;
+  return gemm_w4a4_ws_bytes(m, n, k);
+}
+
+int gemm_w4a4_ws(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                 const void* w_packed, int64_t m, int64_t n, int64_t k, void* y, int y_dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm(w_packed, y, m, n, k, y_dtype);
+  if (st >= 0) return st;
+  if (!a_codes || !a_scales || !a_tensor_scale) return QL_EINVAL;
+  if (!aligned16(a_codes) || !aligned16(a_scales)) return QL_EALIGN;
+  if (workspace) {
+    if (!aligned16(workspace)) return QL_EALIGN;
+    if (workspace_bytes < gemm_w4a4_workspace(m, n, k)) return QL_EWORKSPACE;
+  }
+  return launch_status(launch_gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k,
+                                        y, y_dtype, workspace, workspace_bytes,
+                                        as_stream(stream)));
 }
 
 int gemm_w4a16(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, int64_t k,

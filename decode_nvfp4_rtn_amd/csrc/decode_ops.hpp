@@ -64,18 +64,5 @@ int pick_chunk(int gpw, int cap) {
   return best;
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
-int device_cu_count() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = v;
-  }
-  return cache[dev];
-}
-
 }  // namespace
 }  // namespace qlin

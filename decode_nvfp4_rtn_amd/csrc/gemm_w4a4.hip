@@ -262,21 +262,36 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 
 }  // namespace
 
+namespace {
+
+// The block-cooperative 256x256 kernel holds one block per CU (its LDS double
+// buffer is 160 KiB), so it needs at least one tile per CU; smaller problems
+// take the 128x128 per-wave kernel, which spreads 4x more blocks.  It also
+// addresses activation and weight codes with 31-bit buffer offsets.
+bool use_coop(int64_t m, int64_t n, int64_t k) {
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  const int64_t lim = (int64_t(1) << 31) - (int64_t(1) << 20);
+  return big_tiles >= 256 && m * (k / 2) <= lim && n * (k / 2) <= lim;
+}
+
+}  // namespace
+
+size_t gemm_w4a4_ws_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || !use_coop(m, n, k)) return 0;
+  return coop_split_bytes(coop_split_plan(m, n, k));
+}
+
 hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                             const void* w_packed, int64_t m, int64_t n, int64_t k, void* y,
-                            int y_dtype, hipStream_t s) {
+                            int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {
   const BlobLayout L = blob_layout(0, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
-  // The block-cooperative 256x256 kernel holds one block per CU (its LDS
-  // double buffer is 160 KiB), so it needs at least one tile per CU; smaller
-  // problems take the 128x128 per-wave kernel, which spreads 4x more blocks.
-  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  // the block-cooperative kernel addresses activation and weight codes with
-  // 31-bit buffer offsets
-  const int64_t lim = (int64_t(1) << 31) - (int64_t(1) << 20);
-  const bool offsets_fit = m * (k / 2) <= lim && n * (k / 2) <= lim;
-  if (big_tiles >= 256 && offsets_fit)
-    return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype, s);
+  if (use_coop(m, n, k)) {
+    const size_t need = coop_split_bytes(coop_split_plan(m, n, k));
+    const bool split = need > 0 && ws != nullptr && ws_bytes >= need;
+    return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype,
+                                 static_cast<float*>(ws), split, s);
+  }
   return launch_tile<4, 4>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
 }
 

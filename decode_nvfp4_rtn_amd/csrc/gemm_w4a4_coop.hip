@@ -81,13 +81,25 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int d) {
   return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
+// tile t (0 .. tiles_m * tiles_n - 1, after any XCD remap) -> its origin:
+// groups of GROUP_M m-tiles, n-tiles in order within a group
+__device__ __forceinline__ void coop_tile_origin(int t, int tiles_m, int tiles_n, int& m0,
+                                                 int& n0) {
+  const int in_group = GROUP_M * tiles_n;
+  const int first_m = (t / in_group) * GROUP_M;
+  const int gsz = min(tiles_m - first_m, GROUP_M);
+  m0 = (first_m + (t % in_group) % gsz) * BM;
+  n0 = ((t % in_group) / gsz) * BN;
+}
+
 // WAVES = 4: 2 x 2 waves of 128 x 128 (1 wave per SIMD);
 // WAVES = 8: 2 (n) x 4 (m) waves of 128 x 64 (2 waves per SIMD).
 template <int WAVES, int RS, bool kBF16Out>
 __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
-    int64_t ws_off, int M, int N, int K, void* __restrict__ y) {
+    int64_t ws_off, int M, int N, int K, void* __restrict__ y, int full, int tail, int splits,
+    float* __restrict__ part) {
   constexpr int NTHR = WAVES * 64;
   constexpr int TILE_BYTES = 256 * RS;
   constexpr int WGM = WAVES / 2;          // waves along m
@@ -100,20 +112,29 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // [2][W tile, X tile]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const int total = tiles_m * tiles_n;
-
-  int t = blockIdx.x;
-  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
-  const int in_group = GROUP_M * tiles_n;
-  const int first_m = (t / in_group) * GROUP_M;
-  const int gsz = min(tiles_m - first_m, GROUP_M);
-  const int tm = first_m + (t % in_group) % gsz;
-  const int tn = (t % in_group) / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
 
   const int KT = K / 128;
   const int S = K / BK;
   const int NT16 = N / 16;
+
+  // Blocks [0, full) take whole tiles; blocks past that take one k slice of
+  // one of the `tail` last tiles (slice-major, so the slices of a tile run on
+  // different CUs) and leave an fp32 partial tile for the reduction kernel.
+  int t = blockIdx.x;
+  int st_begin = 0, st_end = S, slot = -1, slice = 0;
+  if (t >= full) {
+    const int u = t - full;
+    slot = u % tail;
+    slice = u / tail;
+    t = full + slot;
+    const int pairs = S / 2;             // the loop advances two stages at a time
+    st_begin = 2 * (slice * pairs / splits);
+    st_end = 2 * ((slice + 1) * pairs / splits);
+  } else if ((full & 7) == 0) {
+    t = (t & 7) * (full >> 3) + (t >> 3);
+  }
+  int m0, n0;
+  coop_tile_origin(t, tiles_m, tiles_n, m0, n0);
 
   // dequantization rows of this thread: row j of 512 = tid + j * NTHR; rows < 256
   // are weight rows n0 + row, the rest activation rows m0 + row - 256 (the same
@@ -188,10 +209,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  gload(ra, 0);
+  gload(ra, st_begin);
 #pragma unroll
   for (int e = 0; e < DW; ++e) dq_store(ra, 0, e);
-  gload(rb, 1);   // S >= 2 (K % 128 == 0)
+  gload(rb, st_begin + 1);   // every range holds an even number >= 2 of stages
   __syncthreads();
 
   const int wn = wave & 1, wm = wave >> 1;
@@ -229,19 +250,30 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   // The prefetches are unconditional (the stage index is clamped; reloading the
   // last stage is harmless): a load under a branch makes the compiler wait for
   // every outstanding load at the join, which would expose the full latency.
-  for (int st = 0; st < S; st += 2) {
+  for (int st = st_begin; st < st_end; st += 2) {
     // even stage: buffer 0; rb holds stage st+1; ra is free -> stage st+2
-    gload(ra, min(st + 2, S - 1));
+    gload(ra, min(st + 2, st_end - 1));
     __builtin_amdgcn_sched_barrier(0);   // issue the prefetch here, not after the stage
     stage(0, rb);
     __syncthreads();
     // odd stage: buffer 1; ra holds stage st+2; rb is free -> stage st+3
-    gload(rb, min(st + 3, S - 1));
+    gload(rb, min(st + 3, st_end - 1));
     __builtin_amdgcn_sched_barrier(0);
     stage(1, ra);
     __syncthreads();
   }
 
+  if (slot >= 0) {
+    // partial tile, unscaled, in the accumulators' own order: each wavefront
+    // store is one contiguous 1 KiB run
+    floatx4* dst = reinterpret_cast<floatx4*>(part) +
+                   (int64_t(slot * splits + slice) * WAVES + wave) * (TN * TM * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) dst[(i * TM + j) * 64] = acc[i][j];
+    return;
+  }
   const float stv = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
@@ -264,11 +296,52 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   }
 }
 
+// Sum of the k slices of one split tile (block = tail slot), in slice order
+// (deterministic), times the tensor scales, stored like the main epilogue.
+template <int WAVES, bool kBF16Out>
+__global__ __launch_bounds__(WAVES * 64) void w4a4_split_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ a_ts,
+    const uint8_t* __restrict__ blob, int M, int N, int full, int splits,
+    void* __restrict__ y) {
+  constexpr int WGM = WAVES / 2, TN = 8, TM = BM / WGM / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = blockIdx.x;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int m0, n0;
+  coop_tile_origin(full + slot, tiles_m, tiles_n, m0, n0);
+  const float stv = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+  const floatx4* src = reinterpret_cast<const floatx4*>(part) +
+                       (int64_t(slot * splits) * WAVES + wave) * (TN * TM * 64) + lane;
+  const int64_t slice_stride = int64_t(WAVES) * TN * TM * 64;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r = lane & 15, q = lane >> 4;
+  for (int i = 0; i < TN; ++i) {
+    const int n = n0 + wn * 128 + i * 16 + 4 * q;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      floatx4 a = src[(i * TM + j) * 64];
+      for (int sl = 1; sl < splits; ++sl) a += src[sl * slice_stride + (i * TM + j) * 64];
+      const int m = m0 + wm * (TM * 16) + j * 16 + r;
+      if (n >= N || m >= M) continue;
+      const floatx4 v = a * stv;
+      if (kBF16Out) {
+        uint2 o;
+        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+      }
+    }
+  }
+}
+
 template <int WAVES, int RS>
 hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                        const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
-                       int64_t k, void* y, int y_dtype, hipStream_t s) {
-  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+                       int64_t k, void* y, int y_dtype, float* part, const CoopSplit& P,
+                       hipStream_t s) {
+  const int blocks = P.full + P.tail * P.splits;
   const size_t lds = 2 * 2 * 256 * RS;
   // the dynamic-LDS limit is a per-function attribute: set it once
   static const hipError_t attr = [lds] {
@@ -281,22 +354,60 @@ hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   }();
   if (attr != hipSuccess) return attr;
   if (y_dtype == 1)
-    w4a4_coop_kernel<WAVES, RS, true><<<tiles, WAVES * 64, lds, s>>>(
-        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y);
+    w4a4_coop_kernel<WAVES, RS, true><<<blocks, WAVES * 64, lds, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y, P.full,
+        P.tail, P.splits, part);
   else
-    w4a4_coop_kernel<WAVES, RS, false><<<tiles, WAVES * 64, lds, s>>>(
-        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y);
+    w4a4_coop_kernel<WAVES, RS, false><<<blocks, WAVES * 64, lds, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y, P.full,
+        P.tail, P.splits, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || P.tail == 0) return e;
+  if (y_dtype == 1)
+    w4a4_split_reduce_kernel<WAVES, true><<<P.tail, WAVES * 64, 0, s>>>(
+        part, a_ts, blob, int(m), int(n), P.full, P.splits, y);
+  else
+    w4a4_split_reduce_kernel<WAVES, false><<<P.tail, WAVES * 64, 0, s>>>(
+        part, a_ts, blob, int(m), int(n), P.full, P.splits, y);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Tiles are dispatched in rounds of one per CU.  When the last round is at
+// most half full, its tiles are split along k into `splits` slices (pairs of
+// stages, at most 8 slices) so that the round occupies the CUs; the slices'
+// fp32 partial tiles are summed by a second launch.  Measured gain where it
+// applies (27B-class o_proj and down at M = 4096, 1.25 rounds) is given in
+// the bench's prefill_27b section.
+CoopSplit coop_split_plan(int64_t m, int64_t n, int64_t k) {
+  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+  const int cus = device_cu_count();
+  CoopSplit P{tiles, 0, 1};
+  if (cus <= 0 || tiles <= cus) return P;
+  const int tail = tiles % cus;
+  if (tail == 0) return P;
+  int splits = cus / tail;
+  const int pairs = static_cast<int>(k / (2 * BK));
+  if (splits > pairs) splits = pairs;
+  if (splits > 8) splits = 8;
+  if (splits < 2) return P;
+  return CoopSplit{tiles - tail, tail, splits};
+}
+
+size_t coop_split_bytes(const CoopSplit& P) {
+  return size_t(P.tail) * P.splits * BM * BN * sizeof(float);
+}
+
 hipError_t launch_gemm_w4a4_coop(const uint8_t* a_codes, const uint8_t* a_scales,
                                  const float* a_ts, const void* w_packed, int64_t m, int64_t n,
-                                 int64_t k, void* y, int y_dtype, hipStream_t s) {
+                                 int64_t k, void* y, int y_dtype, float* part, bool split,
+                                 hipStream_t s) {
   const BlobLayout L = blob_layout(0, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
-  return launch_coop<8, 160>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
+  const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
+  const CoopSplit P = split ? coop_split_plan(m, n, k) : CoopSplit{tiles, 0, 1};
+  return launch_coop<8, 160>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, part, P, s);
 }
 
 }  // namespace qlin

@@ -21,6 +21,19 @@ __device__ __forceinline__ uint2 load_nt8(const void* p) {
   return make_uint2(v[0], v[1]);
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 // ---------------------------------------------------------------------------
 // Packed weight blob: a 256-byte header followed by the data regions.
 // ---------------------------------------------------------------------------
@@ -97,12 +110,25 @@ hipError_t launch_repack(int fmt, int64_t n, int64_t k, const uint8_t* codes,
                          const void* aux, const float* tensor_scale, void* packed,
                          hipStream_t s);
 
+// W4A4: the block-cooperative kernel's last partial round of tiles can be
+// split along k over the idle CUs; `ws` (fp32 partial tiles, may be null)
+// enables that when it holds gemm_w4a4_ws_bytes(m, n, k) bytes.
+size_t gemm_w4a4_ws_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
                             const float* a_ts, const void* w_packed, int64_t m, int64_t n,
-                            int64_t k, void* y, int y_dtype, hipStream_t s);
+                            int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                            hipStream_t s);
+struct CoopSplit {
+  int full;    // tiles computed whole (a multiple of the CU count)
+  int tail;    // tiles of the last partial round, each split along k
+  int splits;  // k slices per tail tile (1: no split)
+};
+CoopSplit coop_split_plan(int64_t m, int64_t n, int64_t k);
+size_t coop_split_bytes(const CoopSplit& plan);
 hipError_t launch_gemm_w4a4_coop(const uint8_t* a_codes, const uint8_t* a_scales,
                                  const float* a_ts, const void* w_packed, int64_t m, int64_t n,
-                                 int64_t k, void* y, int y_dtype, hipStream_t s);
+                                 int64_t k, void* y, int y_dtype, float* part, bool split,
+                                 hipStream_t s);
 hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n,
                              int64_t k, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm_w4a16_sp24(const void* x, const void* w_packed, int64_t m, int64_t n,

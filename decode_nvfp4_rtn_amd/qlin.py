@@ -41,6 +41,8 @@ _SIGS = {
     "repack_weights_bytes": (_sz, [_int, _i64, _i64]),
     "repack_weights": (_int, [_int, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "gemm_w4a4": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "gemm_w4a4_workspace": (_sz, [_i64, _i64, _i64]),
+    "gemm_w4a4_ws": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
     "gemm_w4a16": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "gemm_lut2": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "gemm_w4a16_sp24": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
@@ -186,13 +188,26 @@ def _out(y, m, n, dtype, dev):
     return y, dt
 
 
+def gemm_w4a4_workspace(m, n, k):
+    return _lib.gemm_w4a4_workspace(m, n, k)
+
+
 def gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k, y=None,
-              out_dtype=torch.float32, stream=None):
-    """NVFP4 W4A4 prefill GEMM: Y [m, n] = dequant(A) dequant(W)^T."""
+              out_dtype=torch.float32, stream=None, workspace=None):
+    """NVFP4 W4A4 prefill GEMM: Y [m, n] = dequant(A) dequant(W)^T.
+
+    workspace: None calls gemm_w4a4 (no k split of the last round of tiles);
+    a uint8 GPU tensor of at least gemm_w4a4_workspace(m, n, k) bytes calls
+    gemm_w4a4_ws with it."""
     y, dt = _out(y, m, n, out_dtype, a_codes.device)
-    _check("gemm_w4a4", _lib.gemm_w4a4(
-        _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(w_packed), m, n, k, _ptr(y),
-        dt, _stream(stream)))
+    if workspace is None:
+        _check("gemm_w4a4", _lib.gemm_w4a4(
+            _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(w_packed), m, n, k,
+            _ptr(y), dt, _stream(stream)))
+    else:
+        _check("gemm_w4a4_ws", _lib.gemm_w4a4_ws(
+            _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(w_packed), m, n, k,
+            _ptr(y), dt, _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
 
 

@@ -39,6 +39,8 @@ def lib():
         "repack_weights_bytes": (sz, [i, i64, i64]),
         "repack_weights": (i, [i, i64, i64, vp, vp, vp, vp, sz, vp]),
         "gemm_w4a4": (i, [vp, vp, vp, vp, i64, i64, i64, vp, i, vp]),
+        "gemm_w4a4_workspace": (sz, [i64, i64, i64]),
+        "gemm_w4a4_ws": (i, [vp, vp, vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
         "gemm_w4a16": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
         "gemm_lut2": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
         "gemm_w4a16_sp24": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
@@ -56,7 +58,8 @@ B, C, D, E = 0x20000, 0x30000, 0x40000, 0x50000
 def test_header_declares_the_boundary():
     names = set(_declared())
     for n in ("quantize_nvfp4", "repack_weights", "gemm_w4a4", "gemm_w4a16", "gemm_lut2",
-              "quantize_int4_g128_sp24", "gemm_w4a16_sp24"):
+              "quantize_int4_g128_sp24", "gemm_w4a16_sp24", "gemm_w4a4_workspace",
+              "gemm_w4a4_ws"):
         assert n in names
 
 
@@ -136,3 +139,15 @@ def test_w4a4_validation(lib):
     assert g(A + 1, B, C, D, 64, 256, 512, E, 0, None) == QL_EALIGN
     assert g(A, B + 8, C, D, 64, 256, 512, E, 0, None) == QL_EALIGN
     assert g(A, B, C, D, 0, 256, 512, E, 0, None) == QL_OK
+
+
+def test_w4a4_ws_validation(lib):
+    g = lib.gemm_w4a4_ws
+    assert lib.gemm_w4a4_workspace(0, 256, 512) == 0
+    assert lib.gemm_w4a4_workspace(64, 20, 512) == 0
+    assert lib.gemm_w4a4_workspace(64, 256, 500) == 0
+    assert g(A, B, C, D, 64, 20, 512, E, 0, None, 0, None) == QL_ESHAPE
+    assert g(A, B, C, D, 64, 256, 512, E, 3, None, 0, None) == QL_EDTYPE
+    assert g(A, B, None, D, 64, 256, 512, E, 0, None, 0, None) == QL_EINVAL
+    assert g(A, B, C, D, 64, 256, 512, E, 0, B + 8, 64, None) == QL_EALIGN
+    assert g(A, B, C, D, 0, 256, 512, E, 0, None, 0, None) == QL_OK

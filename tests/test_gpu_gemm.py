@@ -352,3 +352,56 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
     _check(host_f64(y16)[np.ix_(rows, cols)], ref, True)
     # nothing was written past the output: the buffers are exactly [m, n]
     assert y32.shape == (m, n) and y16.shape == (m, n)
+
+
+# ------------------------------ cooperative W4A4, k split of the last round --
+# With a workspace, a last round of tiles that is at most half full is split
+# along k over the idle CUs (fp32 partial tiles, then a fixed-order sum).  The
+# oracle checks a sample; the whole output is compared with the unsplit call
+# (already pinned to the oracle by the tests above), which differs only in the
+# fp32 summation order.
+
+@pytest.mark.parametrize("m,n,k", [
+    (4096, 5120, 5120),   # 27B-class o_proj at M = 4096: 320 tiles
+    (4347, 4096, 2048),   # 17 x 16 tiles, ragged M
+    (4352, 4096, 256),    # K = 256: two stage pairs, so at most two slices
+])
+def test_w4a4_split_last_round(m, n, k):
+    q = require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = ((m + 255) // 256) * ((n + 255) // 256)
+    tail = tiles % cus
+    need = q.gemm_w4a4_workspace(m, n, k)
+    splits = min(cus // tail, k // 128, 8) if 0 < tail else 0
+    if not (tiles > cus and splits >= 2):
+        pytest.skip(f"{tiles} tiles on {cus} CUs: no split applies")
+    assert need == tail * splits * 256 * 256 * 4
+    bits = synth.activations_bf16(12, m, m, k, outliers="channels")
+    w = synth.weights(12, n, n, k)
+    say("w4a4 split last round", m, n, k, tail, splits)
+    blob = _nvfp4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_bf16(bits))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    y32 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.float32, workspace=ws)
+    y16 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16, workspace=ws)
+    y16b = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16, workspace=ws)
+    y32u = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y16b)
+    a, b = host_f64(y32), host_f64(y32u)
+    assert np.max(np.abs(a - b)) <= 1e-4 * np.sqrt(np.mean(b * b))
+    rows = np.unique(np.concatenate([sample_rows(m, 40, m + 1), np.arange(m - 16, m)]))
+    cols = np.unique(np.concatenate([sample_rows(n, 40, n + 2), np.arange(n - 16, n)]))
+    xf = synth.bf16_bits_as_f32(bits)
+    ref = gemm.w4a4(*nvfp4.quantize(xf[rows], s_t=nvfp4.tensor_scale(xf)),
+                    *nvfp4.quantize(w[cols], s_t=nvfp4.tensor_scale(w)))
+    _check(a[np.ix_(rows, cols)], ref, False)
+    _check(host_f64(y16)[np.ix_(rows, cols)], ref, True)
+
+
+def test_w4a4_workspace_not_needed_for_whole_rounds():
+    q = require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # whole rounds of tiles on this device, and a small problem (per-wave kernel)
+    assert q.gemm_w4a4_workspace(256 * cus, 256, 512) == 0
+    assert q.gemm_w4a4_workspace(64, 256, 512) == 0
