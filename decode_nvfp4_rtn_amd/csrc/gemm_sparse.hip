@@ -103,13 +103,17 @@ __device__ __forceinline__ void store_one(void* y, int64_t idx, float v) {
     static_cast<float*>(y)[idx] = v;
 }
 
-// Persistent kernel for one m-tile (M <= 16), K <= 128 * KW * GW and at least
-// two row tiles per block, organised as the dense persistent kernel: wave w
-// owns groups [GW w, GW w + GW) of every row tile and keeps their activation
-// fragments in registers; blocks walk the row tiles with the next tile's
-// weights in flight; four waves add the eight partial sums of a tile.
-template <int GW, bool kBF16Out>
-__global__ __launch_bounds__(KW * 64, KW / 4 * (GW == 2 ? 2 : 1))
+// Persistent kernel for MT m-tiles (M <= 16 MT), K <= 128 * KW * GW and at
+// least two row tiles per block, organised as the dense persistent kernel:
+// wave w owns groups [GW w, GW w + GW) of every row tile and keeps their
+// activation fragments in registers; blocks walk the row tiles with the next
+// tile's weights in flight; 4 MT waves add the eight partial sums of a tile
+// (one component and m-tile each).  The dequantized operand of a group is
+// shared by the m-tiles.
+constexpr int sp_blocks_per_cu(int gw, int mt) { return gw == 2 && mt == 1 ? 2 : 1; }
+
+template <int GW, int MT, bool kBF16Out>
+__global__ __launch_bounds__(KW * 64, KW / 4 * sp_blocks_per_cu(GW, MT))
 void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                          int64_t codes_off, int64_t meta_off, int64_t aux_off, int M, int N,
                          int K, void* __restrict__ y) {
@@ -122,13 +126,16 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   const uint32_t m136 = vconst(0xC308C308u);
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
-  const uint16_t* xr = x + int64_t(min(lane & 15, M - 1)) * K + 16 * (lane >> 4);
 
-  bf16x16_t xh[GW][2];
+  bf16x16_t xh[MT][GW][2];
 #pragma unroll
-  for (int i = 0; i < GW; ++i)
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 16 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) xh[i][s] = load_xh(xr, min(g0 + i, G - 1), s);
+    for (int i = 0; i < GW; ++i)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) xh[mt][i][s] = load_xh(xr, min(g0 + i, G - 1), s);
+  }
 
   struct Tile {
     SpGroup g[GW];
@@ -139,26 +146,31 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     for (int i = 0; i < GW; ++i) sp_load(A.g[i], R, lane, min(g0 + i, G - 1));
   };
 
-  __shared__ float red[2][KW][4][64];
+  __shared__ float red[2][KW][MT][4][64];
   auto finish = [&](const Tile& A, int t, int slot, bool store) {
-    floatx4 acc[GW];
 #pragma unroll
-    for (int i = 0; i < GW; ++i) acc[i] = sp_group(A.g[i], xh[i], neg136, nib_mask, bf16_128);
-    floatx4 tot = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) {
+      floatx4 acc[GW];
 #pragma unroll
-    for (int i = 0; i < GW; ++i) scale_add(tot, acc[i], A.g[i].s, g0 + i < G);
+      for (int i = 0; i < GW; ++i)
+        acc[i] = sp_group(A.g[i], xh[mt][i], neg136, nib_mask, bf16_128);
+      floatx4 tot = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[slot][wave][r][lane] = tot[r];
+      for (int i = 0; i < GW; ++i) scale_add(tot, acc[i], A.g[i].s, g0 + i < G);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[slot][wave][mt][r][lane] = tot[r];
+    }
     __syncthreads();
-    if (wave < 4 && store) {
+    if (wave < 4 * MT && store) {
+      const int mt = wave >> 2, r = wave & 3;
       float v[KW];
 #pragma unroll
-      for (int w = 0; w < KW; ++w) v[w] = red[slot][w][wave][lane];
+      for (int w = 0; w < KW; ++w) v[w] = red[slot][w][mt][r][lane];
 #pragma unroll
       for (int h = KW / 2; h >= 1; h /= 2)
 #pragma unroll
         for (int w = 0; w < h; ++w) v[w] += v[w + h];
-      const int m = lane & 15, n = t * 16 + 4 * (lane >> 4) + wave;
+      const int m = mt * 16 + (lane & 15), n = t * 16 + 4 * (lane >> 4) + r;
       if (m < M) store_one<kBF16Out>(y, int64_t(m) * N + n, v[0]);
     }
   };
@@ -291,18 +303,18 @@ hipError_t launch_sp24_ksplit(const uint16_t* x, const uint8_t* blob, const Blob
 #undef QL_SPK
 }
 
-template <int GW>
+template <int GW, int MT>
 hipError_t launch_sp24_persist(const uint16_t* x, const uint8_t* blob, const BlobLayout& L, int M,
                                int N, int K, void* y, int y_dtype, int cus, hipStream_t s) {
-  const int T = N / 16, per_cu = GW == 2 ? 2 : 1;
+  const int T = N / 16, per_cu = sp_blocks_per_cu(GW, MT);
   // every block owns at least two tiles, and the grid never exceeds T
   const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
   if (y_dtype == 1)
-    sp24_persist_kernel<GW, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.meta_off,
-                                                           L.aux_off, M, N, K, y);
+    sp24_persist_kernel<GW, MT, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.meta_off,
+                                                               L.aux_off, M, N, K, y);
   else
-    sp24_persist_kernel<GW, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.meta_off,
-                                                            L.aux_off, M, N, K, y);
+    sp24_persist_kernel<GW, MT, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.meta_off,
+                                                                L.aux_off, M, N, K, y);
   return hipGetLastError();
 }
 
@@ -315,9 +327,13 @@ hipError_t launch_gemm_w4a16_sp24(const void* x, const void* w_packed, int64_t m
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const int M = int(m), N = int(n), K = int(k), G = int(k / 128), T = int(n / 16);
   const int cus = device_cu_count();
-  if (m <= 16 && G <= KW * 4 && cus > 0 && T >= 2 * cus)
-    return G <= KW * 2 ? launch_sp24_persist<2>(xp, blob, L, M, N, K, y, y_dtype, cus, s)
-                       : launch_sp24_persist<4>(xp, blob, L, M, N, K, y, y_dtype, cus, s);
+  if (m <= 32 && G <= KW * 4 && cus > 0 && T >= 2 * cus) {
+    if (m <= 16)
+      return G <= KW * 2 ? launch_sp24_persist<2, 1>(xp, blob, L, M, N, K, y, y_dtype, cus, s)
+                         : launch_sp24_persist<4, 1>(xp, blob, L, M, N, K, y, y_dtype, cus, s);
+    return G <= KW * 2 ? launch_sp24_persist<2, 2>(xp, blob, L, M, N, K, y, y_dtype, cus, s)
+                       : launch_sp24_persist<4, 2>(xp, blob, L, M, N, K, y, y_dtype, cus, s);
+  }
   const bool wide = T >= 384;   // two row tiles per block still give >= 192 blocks
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = int(m - m0 < 32 ? m - m0 : 32), b = int(m0);
