@@ -25,9 +25,11 @@ lut2     2-bit per-row codebook (K-means, Lloyd iterations).
 gemm     Matrix products on dequantized operands and the pass rule.
 
 Pins (what ties each function to something other than itself) live in
-``tests/test_oracle_*.py``.  ``lut2.fit_lut2`` is pinned only by invariants
-and special cases (no independent library of K-means is available here):
-"parity unpinned" beyond those invariants.
+``tests/test_oracle_*.py``.  ``lut2.lloyd`` is pinned to scikit-learn's
+KMeans (Lloyd's algorithm from the same initial centroids, ten iterations)
+on rows whose clusters all stay populated; its start, tie rule, empty-cluster
+rule, final rounding and re-assignment are pinned by closed forms, brute
+force and special cases.
 """
 
 from . import formats, nvfp4, int4, sparse24, lut2, gemm  # noqa: F401

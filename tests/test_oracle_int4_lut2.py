@@ -162,3 +162,37 @@ def test_lut2_zero_centroid_is_positive_zero():
     assert c[0, 0] == 0 and not np.signbit(c[0, 0])
     idx, cb = lut2.fit(w)
     assert not np.any(cb == 0x8000)
+
+
+def test_lut2_lloyd_matches_scikit_learn_kmeans():
+    """The ten Lloyd iterations from the quantile start are scikit-learn's
+    KMeans(algorithm="lloyd") from the same initial centroids: one init,
+    max_iter=10, tol=0, on the row as one-dimensional data.  Rows are drawn
+    from continuous distributions (no exact ties) and checked to keep every
+    cluster populated, since scikit-learn relocates an empty cluster where
+    this reading keeps its centroid (that rule is pinned separately)."""
+    import warnings
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(35)
+    rows = []
+    for k in (64, 128, 512, 3840):
+        rows.append(rng.standard_normal(k) / np.sqrt(k))                    # the weight recipe
+        rows.append(rng.standard_t(3, k))                                    # heavy tails
+        rows.append(np.concatenate([rng.normal(-1, 0.3, k // 2),
+                                    rng.normal(2, 0.1, k - k // 2)]))       # two modes
+        rows.append(rng.exponential(1.0, k))                                 # one-sided
+    checked = 0
+    for row in rows:
+        w = row.astype(np.float32)[None, :]
+        c_or, _ = lut2.lloyd(w)
+        init = lut2.initial_centroids(w)[0]
+        x = w[0].astype(np.float64)[:, None]
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            km = KMeans(n_clusters=4, init=init[:, None], n_init=1, max_iter=10, tol=0.0,
+                        algorithm="lloyd").fit(x)
+        if np.bincount(km.labels_, minlength=4).min() == 0:
+            continue
+        assert np.allclose(c_or[0], km.cluster_centers_[:, 0], rtol=1e-12, atol=1e-15), row[:4]
+        checked += 1
+    assert checked >= len(rows) - 2
