@@ -21,11 +21,6 @@ constexpr int kPolicyNT = 2;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // A 32-bit constant held in a VGPR, so that two-constant operations such as
 // (w & mask) | bias can use one v_and_or_b32 (VOP3 on this target accepts no
 // literal constants and one scalar operand).

@@ -75,8 +75,8 @@ __device__ __forceinline__ void reduce_store(floatx4 (&tot)[NTB][MT], int nt0, i
     if (m < M && n < N) {
       if (kBF16Out) {
         uint2 o;
-        o.x = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
-        o.y = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
+        o.x = pack_bf16x2(s[0], s[1]);
+        o.y = pack_bf16x2(s[2], s[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
       } else {
         *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = s;
@@ -635,7 +635,7 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
       const int m = mt * 16 + (lane & 15), n = t * 16 + 4 * (lane >> 4) + r;
       if (m < M) {
         if (kBF16Out)
-          static_cast<uint16_t*>(y)[int64_t(m) * N + n] = uint16_t(f32_to_bf16_rne(v[0]));
+          static_cast<uint16_t*>(y)[int64_t(m) * N + n] = to_bf16(v[0]);
         else
           static_cast<float*>(y)[int64_t(m) * N + n] = v[0];
       }

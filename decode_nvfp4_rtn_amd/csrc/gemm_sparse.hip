@@ -98,7 +98,7 @@ __device__ __forceinline__ void scale_add(floatx4& tot, const floatx4& acc, uint
 template <bool kBF16Out>
 __device__ __forceinline__ void store_one(void* y, int64_t idx, float v) {
   if (kBF16Out)
-    static_cast<uint16_t*>(y)[idx] = uint16_t(f32_to_bf16_rne(v));
+    static_cast<uint16_t*>(y)[idx] = to_bf16(v);
   else
     static_cast<float*>(y)[idx] = v;
 }

@@ -72,11 +72,6 @@ __device__ __forceinline__ half2_t scale_h2(uint32_t w4, int g) {
   return half2_t{h, h};
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 __device__ __forceinline__ uint32_t pick(const uint4& v, int d) {
   return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
@@ -286,8 +281,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
       const floatx4 v = acc[i][j] * stv;
       if (kBF16Out) {
         uint2 o;
-        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
       } else {
         *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
@@ -326,8 +321,8 @@ __global__ __launch_bounds__(WAVES * 64) void w4a4_split_reduce_kernel(
       const floatx4 v = a * stv;
       if (kBF16Out) {
         uint2 o;
-        o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-        o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
       } else {
         *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
