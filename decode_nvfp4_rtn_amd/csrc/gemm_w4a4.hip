@@ -86,6 +86,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
     int64_t ws_off, int M, int N, int K, void* __restrict__ y) {
+  if (!blob_matches(blob, 0, N, K)) return;
   constexpr int BN = 32 * WN, BM = 32 * WM;
   constexpr int WU = BN * 4 / kThreads;   // 16-byte W code units per thread per stage
   constexpr int XU = BM * 4 / kThreads;   // 16-byte X code units per thread per stage

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
     const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
     int64_t ws_off, int M, int N, int K, void* __restrict__ y, int full, int tail, int splits,
     float* __restrict__ part) {
+  if (!blob_matches(blob, 0, N, K)) return;   // before any barrier: uniform
   constexpr int NTHR = WAVES * 64;
   constexpr int TILE_BYTES = 256 * RS;
   constexpr int WGM = WAVES / 2;          // waves along m
@@ -296,8 +297,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
 template <int WAVES, bool kBF16Out>
 __global__ __launch_bounds__(WAVES * 64) void w4a4_split_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ a_ts,
-    const uint8_t* __restrict__ blob, int M, int N, int full, int splits,
+    const uint8_t* __restrict__ blob, int M, int N, int K, int full, int splits,
     void* __restrict__ y) {
+  if (!blob_matches(blob, 0, N, K)) return;
   constexpr int WGM = WAVES / 2, TN = 8, TM = BM / WGM / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = blockIdx.x;
@@ -360,10 +362,10 @@ hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   if (e != hipSuccess || P.tail == 0) return e;
   if (y_dtype == 1)
     w4a4_split_reduce_kernel<WAVES, true><<<P.tail, WAVES * 64, 0, s>>>(
-        part, a_ts, blob, int(m), int(n), P.full, P.splits, y);
+        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
   else
     w4a4_split_reduce_kernel<WAVES, false><<<P.tail, WAVES * 64, 0, s>>>(
-        part, a_ts, blob, int(m), int(n), P.full, P.splits, y);
+        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
   return hipGetLastError();
 }
 

@@ -67,6 +67,19 @@ struct BlobHeader {
 };
 static_assert(sizeof(BlobHeader) == 256, "header size");
 
+// Device-side check of a blob against the call's format and shape.  The host
+// cannot read the header without a synchronising copy, so the W4A4 kernels
+// test it first and, on a mismatch, return before any other memory access:
+// a blob packed for another format or shape is never read past its end, and
+// the output is left as it was.  The result is the same for every thread.
+// (The decode kernels do not: there the header read ahead of the first
+// weight loads measured 2-23 % slower on microsecond-long launches.)
+__device__ __forceinline__ bool blob_matches(const uint8_t* blob, int fmt, int n, int k) {
+  const BlobHeader* h = reinterpret_cast<const BlobHeader*>(blob);
+  return h->magic == kBlobMagic && h->version == kBlobVersion && h->fmt == fmt && h->n == n &&
+         h->k == k;
+}
+
 // Region offsets (bytes from the start of the blob), shared by the repacker
 // and the GEMM launchers.
 struct BlobLayout {

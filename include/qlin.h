@@ -186,7 +186,10 @@ int repack_weights(int fmt, int64_t n, int64_t k, const uint8_t *codes,
  * w_packed  NVFP4 blob of W [n, k] from repack_weights.
  * y         out [m, n], y_dtype QL_F32 or QL_BF16 (RNE).
  * Shapes: n % 16 == 0, k % 128 == 0, m >= 0.  n and k must be the values the
- * blob was packed with.  Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EDTYPE,
+ * blob was packed with: the kernels read the blob header first, and a blob
+ * that is not an NVFP4 blob of this (n, k) is not read further and leaves y
+ * untouched (the host cannot detect it without synchronising, so no status
+ * reports it).  Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EDTYPE,
  * QL_EHIP.
  * ---------------------------------------------------------------------- */
 int gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales,
@@ -226,6 +229,10 @@ int gemm_w4a4_ws(const uint8_t *a_codes, const uint8_t *a_scales,
  * y        out [m, n], QL_F32 or QL_BF16.
  * Tuned for m <= 32 (decode batches); any m >= 0 is accepted.
  * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
+ * The blob must be one of this format packed for this (n, k): the decode
+ * kernels read it without checking its header (a header read ahead of the
+ * first weight loads costs 2-23 % on these microsecond launches), so any
+ * other blob is read as if it were one, possibly past its end.
  * ---------------------------------------------------------------------- */
 int gemm_w4a16(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
                int64_t k, void *y, int y_dtype, void *stream);
@@ -237,6 +244,10 @@ int gemm_w4a16(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
  * x        [m, k] bf16.   w_packed: LUT2 blob from repack_weights.
  * y        out [m, n], QL_F32 or QL_BF16.
  * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
+ * The blob must be one of this format packed for this (n, k): the decode
+ * kernels read it without checking its header (a header read ahead of the
+ * first weight loads costs 2-23 % on these microsecond launches), so any
+ * other blob is read as if it were one, possibly past its end.
  * ---------------------------------------------------------------------- */
 int gemm_lut2(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
               int64_t k, void *y, int y_dtype, void *stream);
@@ -249,6 +260,10 @@ int gemm_lut2(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
  * y        out [m, n], QL_F32 or QL_BF16.
  * Tuned for m <= 32; any m >= 0 is accepted.
  * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
+ * The blob must be one of this format packed for this (n, k): the decode
+ * kernels read it without checking its header (a header read ahead of the
+ * first weight loads costs 2-23 % on these microsecond launches), so any
+ * other blob is read as if it were one, possibly past its end.
  * ---------------------------------------------------------------------- */
 int gemm_w4a16_sp24(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
                     int64_t k, void *y, int y_dtype, void *stream);

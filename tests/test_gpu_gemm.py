@@ -405,3 +405,34 @@ def test_w4a4_workspace_not_needed_for_whole_rounds():
     # whole rounds of tiles on this device, and a small problem (per-wave kernel)
     assert q.gemm_w4a4_workspace(256 * cus, 256, 512) == 0
     assert q.gemm_w4a4_workspace(64, 256, 512) == 0
+
+
+# ------------------------------------------------------------ blob guard --
+# The host cannot read a blob's header without a synchronising copy, so the
+# W4A4 kernels check it (magic, version, format, n, k) before any other access
+# and return on a mismatch: the output keeps its previous contents and no byte
+# past the blob is read.  (The decode kernels take the blob on trust; their
+# contract says so.)
+
+def test_w4a4_blob_guard_leaves_output_untouched():
+    q = require_gpu()
+    n, k, m = 256, 512, 4
+    w = synth.weights(13, 0, n, k)
+    nv, i4, l2 = _nvfp4_blob(q, w), _int4_blob(q, w), _lut2_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_f32(synth.activations(13, 0, m, k)))
+    say("w4a4 blob guard")
+    cases = [
+        ("an INT4 blob", n, lambda y: q.gemm_w4a4(ac, as_, at, i4, m, n, k, y=y)),
+        ("a LUT2 blob", n, lambda y: q.gemm_w4a4(ac, as_, at, l2, m, n, k, y=y)),
+        ("n below the packed n", n - 16, lambda y: q.gemm_w4a4(ac, as_, at, nv, m, n - 16, k, y=y)),
+        ("k below the packed k", n, lambda y: q.gemm_w4a4(ac, as_, at, nv, m, n, 256, y=y)),
+    ]
+    for name, nn, fn in cases:
+        y = torch.full((m, nn), 7.0, dtype=torch.float32, device="cuda")
+        fn(y)
+        torch.cuda.synchronize()
+        assert torch.all(y == 7.0), name
+    y = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
+    q.gemm_w4a4(ac, as_, at, nv, m, n, k, y=y)
+    torch.cuda.synchronize()
+    assert not torch.any(y == 7.0)
