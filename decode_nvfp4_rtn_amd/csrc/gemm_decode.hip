@@ -663,13 +663,11 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
 // instantiation that needs more than the default 64 KiB.
 template <int GW, int MT, bool kLut, bool kBF16Out>
 hipError_t persist_lds_attr() {
-  static const hipError_t e =
-      persist_lds_bytes(GW, MT, kLut) > 65536
-          ? hipFuncSetAttribute(
-                reinterpret_cast<const void*>(decode_persist_kernel<GW, MT, kLut, kBF16Out>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, int(persist_lds_bytes(GW, MT, kLut)))
-          : hipSuccess;
-  return e;
+  static std::atomic<int> done[64];
+  if (persist_lds_bytes(GW, MT, kLut) <= 65536) return hipSuccess;
+  return lds_limit_once(done,
+                        reinterpret_cast<const void*>(decode_persist_kernel<GW, MT, kLut, kBF16Out>),
+                        int(persist_lds_bytes(GW, MT, kLut)));
 }
 
 template <bool kLut, int MT, int NTB, int WMAX, int KWT>

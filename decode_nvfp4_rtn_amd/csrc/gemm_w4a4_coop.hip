@@ -340,15 +340,14 @@ hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const fl
                        hipStream_t s) {
   const int blocks = P.full + P.tail * P.splits;
   const size_t lds = 2 * 2 * 256 * RS;
-  // the dynamic-LDS limit is a per-function attribute: set it once
-  static const hipError_t attr = [lds] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_coop_kernel<WAVES, RS, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(w4a4_coop_kernel<WAVES, RS, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    return e;
-  }();
+  // the dynamic-LDS limit is a per-kernel, per-device attribute
+  static std::atomic<int> done_bf16[64], done_f32[64];
+  const hipError_t attr =
+      y_dtype == 1
+          ? lds_limit_once(done_bf16, reinterpret_cast<const void*>(w4a4_coop_kernel<WAVES, RS, true>),
+                           int(lds))
+          : lds_limit_once(done_f32, reinterpret_cast<const void*>(w4a4_coop_kernel<WAVES, RS, false>),
+                           int(lds));
   if (attr != hipSuccess) return attr;
   if (y_dtype == 1)
     w4a4_coop_kernel<WAVES, RS, true><<<blocks, WAVES * 64, lds, s>>>(

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 namespace qlin {
 
 // Streaming (non-temporal) vector loads: data read once should not displace
@@ -22,16 +24,31 @@ __device__ __forceinline__ uint2 load_nt8(const void* p) {
 }
 
 // Compute units of the current device (cached per device; 0 if unknown).
+// Host threads may call concurrently: the cache slots are atomics (a race
+// only repeats the attribute query, which returns the same value).
 inline int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
+}
+
+// Raise a kernel's dynamic-LDS limit on the current device, once per device
+// (`done` is the caller's per-kernel flag array of 64 devices).  Host threads
+// may race here; that only repeats the call.
+inline hipError_t lds_limit_once(std::atomic<int>* done, const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && dev >= 0 && dev < 64) done[dev].store(1, std::memory_order_release);
+  return e;
 }
 
 // fp32 -> bf16, round to nearest even, with v_cvt_pk_bf16_f32 (two values
