@@ -182,10 +182,40 @@ def repack_weights(fmt, n, k, codes, scales_or_lut, tensor_scale=None, packed=No
 def _out(y, m, n, dtype, dev):
     if y is None:
         y = torch.empty((m, n), dtype=dtype, device=dev)
+    else:
+        _dev(y, "y")
+        if tuple(y.shape) != (m, n):
+            raise ValueError(f"y must be [{m}, {n}], got {list(y.shape)}")
     dt = {torch.float32: QL_F32, torch.bfloat16: QL_BF16}.get(y.dtype)
     if dt is None:
         raise ValueError("y must be float32 or bfloat16")
     return y, dt
+
+
+# Host-side shape and size checks (no device access, no synchronisation).
+# Every buffer a kernel reads or writes must be at least as large as the call
+# says; in particular a packed blob must hold repack_weights_bytes(fmt, n, k)
+# bytes, so no kernel reads past it whatever its contents.
+
+def _typed(t, name, dtype):
+    _dev(t, name)
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _rows(t, name, dtype, m, cols):
+    _typed(t, name, dtype)
+    if t.dim() != 2 or t.shape[1] != cols or t.shape[0] < m:
+        raise ValueError(f"{name} must be [>= {m}, {cols}], got {list(t.shape)}")
+
+
+def _blob(w_packed, fmt, n, k):
+    _typed(w_packed, "w_packed", torch.uint8)
+    need = _lib.repack_weights_bytes(fmt, n, k)
+    if w_packed.numel() < need:
+        raise ValueError(f"w_packed holds {w_packed.numel()} bytes; a format-{fmt} blob "
+                         f"of [{n}, {k}] takes {need}")
 
 
 def gemm_w4a4_workspace(m, n, k):
@@ -199,7 +229,15 @@ def gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k, y=None,
     workspace: None calls gemm_w4a4 (no k split of the last round of tiles);
     a uint8 GPU tensor of at least gemm_w4a4_workspace(m, n, k) bytes calls
     gemm_w4a4_ws with it."""
+    _rows(a_codes, "a_codes", torch.uint8, m, k // 2)
+    _rows(a_scales, "a_scales", torch.uint8, m, k // 16)
+    _typed(a_tensor_scale, "a_tensor_scale", torch.float32)
+    if a_tensor_scale.numel() < 1:
+        raise ValueError("a_tensor_scale must hold one value")
+    _blob(w_packed, QL_NVFP4, n, k)
     y, dt = _out(y, m, n, out_dtype, a_codes.device)
+    if workspace is not None:
+        _typed(workspace, "workspace", torch.uint8)
     if workspace is None:
         _check("gemm_w4a4", _lib.gemm_w4a4(
             _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(w_packed), m, n, k,
@@ -213,8 +251,9 @@ def gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k, y=None,
 
 def gemm_w4a16(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
     """W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times INT4-g128 weights^T."""
-    _dev(x, "x")
-    m = x.shape[0]
+    m = x.shape[0] if x.dim() == 2 else -1
+    _rows(x, "x", torch.bfloat16, m, k)
+    _blob(w_packed, QL_INT4_G128, n, k)
     y, dt = _out(y, m, n, out_dtype, x.device)
     _check("gemm_w4a16", _lib.gemm_w4a16(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
                                          _stream(stream)))
@@ -223,8 +262,9 @@ def gemm_w4a16(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None)
 
 def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
     """LUT2 decode GEMM: Y [m, n] = X bf16 [m, k] times codebook weights^T."""
-    _dev(x, "x")
-    m = x.shape[0]
+    m = x.shape[0] if x.dim() == 2 else -1
+    _rows(x, "x", torch.bfloat16, m, k)
+    _blob(w_packed, QL_LUT2, n, k)
     y, dt = _out(y, m, n, out_dtype, x.device)
     _check("gemm_lut2", _lib.gemm_lut2(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
                                        _stream(stream)))
@@ -233,8 +273,9 @@ def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
 
 def gemm_w4a16_sp24(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
     """2:4 sparse W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times 2:4 INT4 weights^T."""
-    _dev(x, "x")
-    m = x.shape[0]
+    m = x.shape[0] if x.dim() == 2 else -1
+    _rows(x, "x", torch.bfloat16, m, k)
+    _blob(w_packed, QL_INT4_SP24, n, k)
     y, dt = _out(y, m, n, out_dtype, x.device)
     _check("gemm_w4a16_sp24", _lib.gemm_w4a16_sp24(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
                                                    _stream(stream)))

@@ -421,11 +421,19 @@ def test_w4a4_blob_guard_leaves_output_untouched():
     nv, i4, l2 = _nvfp4_blob(q, w), _int4_blob(q, w), _lut2_blob(q, w)
     ac, as_, at = q.quantize_nvfp4(dev_f32(synth.activations(13, 0, m, k)))
     say("w4a4 blob guard")
+    # through the C ABI: the Python binding would reject most of these calls
+    # on the host already (blob size, operand shapes)
+    lib = q.raw()
+
+    def raw_call(blob, nn, kk, y):
+        st = lib.gemm_w4a4(ac.data_ptr(), as_.data_ptr(), at.data_ptr(), blob.data_ptr(), m, nn,
+                           kk, y.data_ptr(), q.QL_F32, torch.cuda.current_stream().cuda_stream)
+        assert st == q.QL_OK, st
     cases = [
-        ("an INT4 blob", n, lambda y: q.gemm_w4a4(ac, as_, at, i4, m, n, k, y=y)),
-        ("a LUT2 blob", n, lambda y: q.gemm_w4a4(ac, as_, at, l2, m, n, k, y=y)),
-        ("n below the packed n", n - 16, lambda y: q.gemm_w4a4(ac, as_, at, nv, m, n - 16, k, y=y)),
-        ("k below the packed k", n, lambda y: q.gemm_w4a4(ac, as_, at, nv, m, n, 256, y=y)),
+        ("an INT4 blob", n, lambda y: raw_call(i4, n, k, y)),
+        ("a LUT2 blob", n, lambda y: raw_call(l2, n, k, y)),
+        ("n below the packed n", n - 16, lambda y: raw_call(nv, n - 16, k, y)),
+        ("k below the packed k", n, lambda y: raw_call(nv, n, 256, y)),
     ]
     for name, nn, fn in cases:
         y = torch.full((m, nn), 7.0, dtype=torch.float32, device="cuda")
@@ -436,3 +444,29 @@ def test_w4a4_blob_guard_leaves_output_untouched():
     q.gemm_w4a4(ac, as_, at, nv, m, n, k, y=y)
     torch.cuda.synchronize()
     assert not torch.any(y == 7.0)
+
+
+def test_binding_rejects_undersized_buffers():
+    """The Python binding checks operand shapes and blob sizes on the host, so
+    a too-small buffer never reaches a kernel."""
+    q = require_gpu()
+    n, k, m = 256, 512, 4
+    w = synth.weights(14, 0, n, k)
+    nv, i4 = _nvfp4_blob(q, w), _int4_blob(q, w)
+    ac, as_, at = q.quantize_nvfp4(dev_f32(synth.activations(14, 0, m, k)))
+    xb = dev_bf16(synth.decode_x_bf16(14, 0, m, k))
+    say("binding size checks")
+    bad = [
+        lambda: q.gemm_w4a4(ac, as_, at, i4, m, n, k),                     # INT4 blob is too small
+        lambda: q.gemm_w4a4(ac, as_, at, nv, m, n + 16, k),                # blob for a smaller n
+        lambda: q.gemm_w4a4(ac[:, :128].contiguous(), as_, at, nv, m, n, k),
+        lambda: q.gemm_w4a4(ac, as_, at, nv, m + 1, n, k),                 # fewer rows than m
+        lambda: q.gemm_w4a4(ac, as_, at, nv, m, n, k, y=torch.empty((m, n - 16), device="cuda")),
+        lambda: q.gemm_w4a16(xb, i4, n + 16, k),
+        lambda: q.gemm_w4a16(xb[:, :256].contiguous(), i4, n, k),
+        lambda: q.gemm_lut2(xb, i4[:1024], n, k),
+        lambda: q.gemm_w4a16_sp24(xb.float(), i4, n, k),                   # fp32 activations
+    ]
+    for fn in bad:
+        with pytest.raises(ValueError):
+            fn()
