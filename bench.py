@@ -84,9 +84,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each GPU would run the same kernels on its 1/N share of N; see DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (sharded by "
+              "output columns, each GPU would run the same kernels on its 1/N share of the "
+              "weight rows).", file=sys.stderr)
         sys.exit(2)
 
     import torch
