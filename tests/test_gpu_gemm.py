@@ -363,6 +363,7 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [
     (4096, 5120, 5120),   # 27B-class o_proj at M = 4096: 320 tiles
+    (4096, 5120, 17408),  # 27B-class down at M = 4096 (the benchmarked split shapes)
     (4347, 4096, 2048),   # 17 x 16 tiles, ragged M
     (4352, 4096, 256),    # K = 256: two stage pairs, so at most two slices
 ])
