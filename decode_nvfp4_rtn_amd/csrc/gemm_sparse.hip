@@ -30,6 +30,7 @@ namespace {
 
 typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // B operand of the 64-k half s of group g (xr already points at row and
 // k offset 16 (lane / 16)): 16 consecutive bf16, two 16-byte loads
@@ -48,26 +49,25 @@ struct SpGroup {
 };
 
 struct SpRsrc {
-  __amdgpu_buffer_rsrc_t c, m, s;
+  __amdgpu_buffer_rsrc_t c, s;
 };
 
 // buffer resources of row tile t: scalar tile and group offsets
-__device__ __forceinline__ SpRsrc sp_rsrc(const uint8_t* blob, int64_t codes_off, int64_t meta_off,
-                                          int64_t aux_off, int64_t t, int G) {
+__device__ __forceinline__ SpRsrc sp_rsrc(const uint8_t* blob, int64_t codes_off, int64_t aux_off,
+                                          int64_t t, int G) {
   SpRsrc R;
-  R.c = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob + codes_off + t * G * 512), 0,
-                                          G * 512, kRsrcWord3);
-  R.m = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob + meta_off + t * G * 256), 0,
-                                          G * 256, kRsrcWord3);
+  R.c = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob + codes_off + t * G * 768), 0,
+                                          G * 768, kRsrcWord3);
   R.s = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blob + aux_off + t * G * 32), 0,
                                           G * 32, kRsrcWord3);
   return R;
 }
 
+// codes and positions of this lane in one 12-byte load, then the scales
 __device__ __forceinline__ void sp_load(SpGroup& A, const SpRsrc& R, int lane, int gc) {
-  const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(R.c, lane * 8, gc * 512, kPolicyNT);
+  const u32x3 c = __builtin_amdgcn_raw_buffer_load_b96(R.c, lane * 12, gc * 768, kPolicyNT);
   A.c = make_uint2(c[0], c[1]);
-  A.m = __builtin_amdgcn_raw_buffer_load_b32(R.m, lane * 4, gc * 256, kPolicyNT);
+  A.m = c[2];
   const u32x2 s = __builtin_amdgcn_raw_buffer_load_b64(R.s, (lane >> 4) * 8, gc * 32, 0);
   A.s = make_uint2(s[0], s[1]);
 }
@@ -115,8 +115,8 @@ constexpr int sp_blocks_per_cu(int gw, int mt) { return gw == 2 && mt == 1 ? 2 :
 template <int GW, int MT, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64, KW / 4 * sp_blocks_per_cu(GW, MT))
 void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
-                         int64_t codes_off, int64_t meta_off, int64_t aux_off, int M, int N,
-                         int K, void* __restrict__ y) {
+                         int64_t codes_off, int64_t aux_off, int M, int N, int K,
+                         void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
@@ -141,7 +141,7 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     SpGroup g[GW];
   };
   auto load = [&](Tile& A, int t) {
-    const SpRsrc R = sp_rsrc(blob, codes_off, meta_off, aux_off, t, G);
+    const SpRsrc R = sp_rsrc(blob, codes_off, aux_off, t, G);
 #pragma unroll
     for (int i = 0; i < GW; ++i) sp_load(A.g[i], R, lane, min(g0 + i, G - 1));
   };
@@ -199,7 +199,7 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
 template <int MT, int NTB, int WMAX, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob, int64_t codes_off,
-    int64_t meta_off, int64_t aux_off, int M, int m0, int N, int K, void* __restrict__ y) {
+    int64_t aux_off, int M, int m0, int N, int K, void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
   SpRsrc R[NTB];
 #pragma unroll
   for (int nt = 0; nt < NTB; ++nt)
-    R[nt] = sp_rsrc(blob, codes_off, meta_off, aux_off, min(nt0 + nt, T - 1), G);
+    R[nt] = sp_rsrc(blob, codes_off, aux_off, min(nt0 + nt, T - 1), G);
 
   floatx4 tot[NTB][MT];
 #pragma unroll
@@ -288,10 +288,10 @@ hipError_t launch_sp24_ksplit(const uint16_t* x, const uint8_t* blob, const Blob
   {                                                                                         \
     if (y_dtype == 1)                                                                       \
       sp24_ksplit_kernel<MT, NTB, cmin(W, kCap), true><<<blocks, KW * 64, 0, s>>>(          \
-          x, blob, L.codes_off, L.meta_off, L.aux_off, M, m0, N, K, y);                     \
+          x, blob, L.codes_off, L.aux_off, M, m0, N, K, y);                     \
     else                                                                                    \
       sp24_ksplit_kernel<MT, NTB, cmin(W, kCap), false><<<blocks, KW * 64, 0, s>>>(         \
-          x, blob, L.codes_off, L.meta_off, L.aux_off, M, m0, N, K, y);                     \
+          x, blob, L.codes_off, L.aux_off, M, m0, N, K, y);                     \
     return hipGetLastError();                                                               \
   }
   switch (pick_chunk((K / 128 + KW - 1) / KW, kCap)) {
@@ -310,11 +310,11 @@ hipError_t launch_sp24_persist(const uint16_t* x, const uint8_t* blob, const Blo
   // every block owns at least two tiles, and the grid never exceeds T
   const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
   if (y_dtype == 1)
-    sp24_persist_kernel<GW, MT, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.meta_off,
-                                                               L.aux_off, M, N, K, y);
+    sp24_persist_kernel<GW, MT, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.aux_off,
+                                                               M, N, K, y);
   else
-    sp24_persist_kernel<GW, MT, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.meta_off,
-                                                                L.aux_off, M, N, K, y);
+    sp24_persist_kernel<GW, MT, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.aux_off,
+                                                                M, N, K, y);
   return hipGetLastError();
 }
 

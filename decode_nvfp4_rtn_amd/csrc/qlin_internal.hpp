@@ -69,7 +69,7 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 // Packed weight blob: a 256-byte header followed by the data regions.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kBlobMagic = 0x4E494C51u;  // "QLIN"
-constexpr int kBlobVersion = 1;
+constexpr int kBlobVersion = 2;   // 2: 2:4 codes and positions interleaved
 constexpr size_t kHeaderBytes = 256;
 
 struct BlobHeader {
@@ -102,7 +102,6 @@ __device__ __forceinline__ bool blob_matches(const uint8_t* blob, int fmt, int n
 struct BlobLayout {
   size_t codes_off, codes_bytes;
   size_t aux_off, aux_bytes;    // scales or codebook
-  size_t meta_off, meta_bytes;  // 2:4 sparse INT4 only: kept positions (else 0)
   size_t total;
 };
 
@@ -117,20 +116,15 @@ inline BlobLayout blob_layout(int fmt, int64_t n, int64_t k) {
   } else if (fmt == 1) {   // INT4 g128: codes n*k/2, bf16 scales n*k/128*2
     L.codes_bytes = size_t(n) * k / 2;
     L.aux_bytes = size_t(n) * (k / 128) * 2;
-  } else if (fmt == 3) {   // 2:4 INT4 g128: kept codes n*k/4, positions n*k/8, scales
-    L.codes_bytes = size_t(n) * k / 4;
-    L.meta_bytes = size_t(n) * k / 8;
+  } else if (fmt == 3) {   // 2:4 INT4 g128: kept codes n*k/4 interleaved with their
+                           // positions n*k/8 (12 bytes per lane), scales
+    L.codes_bytes = size_t(n) * k * 3 / 8;
     L.aux_bytes = size_t(n) * (k / 128) * 2;
   } else {                 // LUT2: indices n*k/4, codebook 8 bytes per row
     L.codes_bytes = size_t(n) * k / 4;
     L.aux_bytes = size_t(n) * 8;
   }
-  size_t end = L.codes_off + L.codes_bytes;
-  if (L.meta_bytes) {
-    L.meta_off = align256(end);
-    end = L.meta_off + L.meta_bytes;
-  }
-  L.aux_off = align256(end);
+  L.aux_off = align256(L.codes_off + L.codes_bytes);
   L.total = align256(L.aux_off + L.aux_bytes);
   return L;
 }

@@ -22,13 +22,14 @@
 //   scales [nt][ks][16 rows] bf16
 // 2:4 sparse INT4 group-128 (Sparse-MARLIN reading, W4A16 decode on the
 // gfx950 2:4 sparse MFMA v_smfmac_f32_16x16x64_bf16):
-//   codes  [nt][ks][64 lanes][8 B]  dword s (0, 1) covers k = 128 ks + 64 s +
-//          16 (2 (q % 2) + h) + 8 (q / 2) + 4 b + p for quads g = 2 h + b
-//          (h, b in {0, 1}) and p = 0..3; element 2g holds the code at the
-//          lower kept position p0 of quad g, element 2g+1 the one at p1, with
-//          element e at bits 4 (e/2) (e even) or 16 + 4 (e/2) (e odd)
-//   meta   [nt][ks][64 lanes][4 B]  the kept positions: p of element e of
-//          dword s at bits 16 s + 2 e (the sparse MFMA's index operand)
+//   codes  [nt][ks][64 lanes][12 B]: dwords 0 and 1 are the kept codes,
+//          dword s (0, 1) covering k = 128 ks + 64 s + 16 (2 (q % 2) + h) +
+//          8 (q / 2) + 4 b + p for quads g = 2 h + b (h, b in {0, 1}) and
+//          p = 0..3; element 2g holds the code at the lower kept position p0
+//          of quad g, element 2g+1 the one at p1, with element e at bits
+//          4 (e/2) (e even) or 16 + 4 (e/2) (e odd).  Dword 2 holds the kept
+//          positions: p of element e of half s at bits 16 s + 2 e (the sparse
+//          MFMA's index operand).  One 12-byte load per lane and group.
 //   scales [nt][ks][16 rows] bf16
 //   Kept per quad: the two codes of largest |q| (ties to the lower column),
 //   i.e. every nonzero code when the codes come from the 2:4 quantizer.
@@ -170,7 +171,7 @@ __global__ void repack_lut2_book(const uint16_t* __restrict__ cent, int64_t n,
 // 2:4 INT4: one thread per (lane, 128-k step) writes its 8 code bytes and
 // its 4 position bytes.
 __global__ void repack_sp24(const uint8_t* __restrict__ codes, int64_t n, int64_t k,
-                            uint2* __restrict__ out_codes, uint32_t* __restrict__ out_meta) {
+                            uint32_t* __restrict__ out) {
   const int64_t units = n * k / 32;
   const int64_t KT = k / 128;
   for (int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; u < units;
@@ -203,8 +204,9 @@ __global__ void repack_sp24(const uint8_t* __restrict__ codes, int64_t n, int64_
         cw[s] |= (uq[pos[0]] << (4 * g)) | (uq[pos[1]] << (16 + 4 * g));
         meta |= (uint32_t(pos[0]) << (16 * s + 4 * g)) | (uint32_t(pos[1]) << (16 * s + 4 * g + 2));
       }
-    out_codes[u] = make_uint2(cw[0], cw[1]);
-    out_meta[u] = meta;
+    out[3 * u] = cw[0];
+    out[3 * u + 1] = cw[1];
+    out[3 * u + 2] = meta;
   }
 }
 
@@ -231,8 +233,7 @@ hipError_t launch_repack(int fmt, int64_t n, int64_t k, const uint8_t* codes, co
           codes, n, k, reinterpret_cast<uint32_t*>(base + L.codes_off));
     else
       repack_sp24<<<grid_for(n * k / 32), 256, 0, s>>>(
-          codes, n, k, reinterpret_cast<uint2*>(base + L.codes_off),
-          reinterpret_cast<uint32_t*>(base + L.meta_off));
+          codes, n, k, reinterpret_cast<uint32_t*>(base + L.codes_off));
     repack_int4_scales<<<grid_for(n * (k / 128)), 256, 0, s>>>(
         static_cast<const uint16_t*>(aux), n, k, reinterpret_cast<uint16_t*>(base + L.aux_off));
   } else {
