@@ -43,21 +43,31 @@ def _progress(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def _traffic_record(kernel_src):
-    """HBM traffic of the dominant kernel from the committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel source (hash match)."""
+def _kernel_build_hash():
+    """Hash of what decides the block-cooperative GEMM's machine code: its
+    source, the internal header it includes, and its compile flags."""
     import hashlib
+    from decode_nvfp4_rtn_amd import build as qbuild
+    h = hashlib.sha256()
+    for name in ("gemm_w4a4_coop.hip", "qlin_internal.hpp"):
+        h.update(open(os.path.join(qbuild.CSRC, name), "rb").read())
+    h.update(" ".join(qbuild.COMMON + qbuild.SOURCES["gemm_w4a4_coop.hip"]).encode())
+    return h.hexdigest()[:16]
+
+
+def _traffic_record():
+    """HBM traffic of the dominant kernel from the committed rocprofv3 --pmc
+    summary, if it was taken on the kernel as built now (hash match)."""
     path = os.path.join(ROOT, "profiles", "gemm_w4a4_qwen3_traffic.md")
     if not os.path.exists(path):
         return None
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
     rec = {}
     for line in open(path):
         if line.startswith("traffic:"):
             for kv in line.split()[1:]:
                 k, v = kv.split("=")
                 rec[k] = v
-    if rec.get("source_sha256_16") != h:
+    if rec.get("kernel_sha256_16") != _kernel_build_hash():
         return None
     return float(rec["bytes_per_launch"])
 
@@ -511,7 +521,7 @@ def main():
         cpu = cpu_baseline(args.cpu_rows, pre, M)
         _progress(f"cpu baseline: {cpu['sample']}")
 
-    traffic = _traffic_record(os.path.join(ROOT, "decode_nvfp4_rtn_amd", "csrc", "gemm_w4a4_coop.hip"))
+    traffic = _traffic_record()
     avg_launch_ms = gemm_ms_step / len(P)
     out = {
         "metric": METRIC,

@@ -10,7 +10,11 @@ into ``decode_nvfp4_rtn_amd/libqlin.so``.  Flags:
 * no fast-math anywhere: divisions stay correctly rounded and denormals are
   kept;
 * ``-ffp-contract=off`` for the quantizers, so no multiply is fused into an
-  add and every binary32 step rounds once.
+  add and every binary32 step rounds once;
+* the W4A4 block-cooperative GEMM is scheduled with the compiler's
+  memory-clause strategy, which keeps its loads and LDS reads in tighter
+  groups: 0.5-3.3 % faster over the Qwen3-8B-like and 27B-class prefill
+  shapes (interleaved timing in one process, outputs bit-identical).
 """
 
 import os
@@ -30,7 +34,7 @@ SOURCES = {
     "weight_prep.hip": ["-ffp-contract=off"],
     "repack.hip": [],
     "gemm_w4a4.hip": [],
-    "gemm_w4a4_coop.hip": [],
+    "gemm_w4a4_coop.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     "gemm_decode.hip": [],
     "gemm_sparse.hip": [],
 }
