@@ -81,6 +81,24 @@ def _dev(t, name):
     return t
 
 
+def _bytes(t, name, nbytes, dtype=None):
+    """t is a contiguous GPU tensor (of dtype, if given) of at least nbytes bytes."""
+    _dev(t, name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes; the call needs {nbytes}")
+    return t
+
+
+def _matrix(t, name, dtype):
+    _dev(t, name)
+    if t.dtype != dtype or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D {dtype} tensor, got {t.dim()}-D {t.dtype}")
+    return t.shape
+
+
 def ql_status_str(status):
     return _lib.ql_status_str(status).decode()
 
@@ -103,6 +121,8 @@ def quantize_nvfp4(x, tensor_scale=None, codes=None, scales=None, workspace=None
     Returns (codes uint8 [rows, cols/2], scales uint8 [rows, cols/16], s_t fp32 [1]).
     """
     _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D, got {x.dim()}-D")
     rows, cols = x.shape
     dt = {torch.float32: QL_F32, torch.bfloat16: QL_BF16}.get(x.dtype)
     if dt is None:
@@ -110,17 +130,22 @@ def quantize_nvfp4(x, tensor_scale=None, codes=None, scales=None, workspace=None
     dev = x.device
     if codes is None:
         codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    _bytes(codes, "codes", rows * (cols // 2), torch.uint8)
     if scales is None:
         scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    _bytes(scales, "scales", rows * (cols // 16), torch.uint8)
     flags = 0
     if tensor_scale is None:
         ts = ts_out if ts_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+        _bytes(ts, "ts_out", 4, torch.float32)
     else:
-        ts = _dev(tensor_scale, "tensor_scale")
+        ts = _bytes(tensor_scale, "tensor_scale", 4, torch.float32)
         flags = QL_STATIC_SCALE
     wsb = _lib.quantize_nvfp4_workspace(rows, cols)
     if workspace is None and not flags:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _bytes(workspace, "workspace", 0, torch.uint8)
     _check("quantize_nvfp4", _lib.quantize_nvfp4(
         _ptr(x), dt, rows, cols, _ptr(codes), _ptr(scales), _ptr(ts), flags,
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
@@ -131,12 +156,13 @@ def quantize_int4_g128(w, codes=None, scales=None, stream=None, sparse24=False):
     """Symmetric INT4 group-128 quantization of fp32 weights [n, k]; with
     sparse24, 2:4 magnitude pruning along k first (quantize_int4_g128_sp24).
     Returns (codes uint8 [n, k/2], scales int16 (bf16 bits) [n, k/128])."""
-    _dev(w, "w")
-    n, k = w.shape
+    n, k = _matrix(w, "w", torch.float32)
     if codes is None:
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    _bytes(codes, "codes", n * (k // 2), torch.uint8)
     if scales is None:
         scales = torch.empty((n, k // 128), dtype=torch.int16, device=w.device)
+    _bytes(scales, "scales", n * (k // 128) * 2)
     name = "quantize_int4_g128_sp24" if sparse24 else "quantize_int4_g128"
     _check(name, getattr(_lib, name)(_ptr(w), n, k, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
@@ -149,18 +175,29 @@ def fit_lut2_workspace(n, k):
 def fit_lut2(w, idx=None, centroids=None, workspace=None, stream=None):
     """2-bit codebook fit of fp32 weights [n, k] (10 Lloyd iterations per row).
     Returns (idx uint8 [n, k/4], centroids int16 (bf16 bits) [n, 4])."""
-    _dev(w, "w")
-    n, k = w.shape
+    n, k = _matrix(w, "w", torch.float32)
     if idx is None:
         idx = torch.empty((n, k // 4), dtype=torch.uint8, device=w.device)
+    _bytes(idx, "idx", n * (k // 4), torch.uint8)
     if centroids is None:
         centroids = torch.empty((n, 4), dtype=torch.int16, device=w.device)
+    _bytes(centroids, "centroids", n * 8)
     wsb = _lib.fit_lut2_workspace(n, k)
     if workspace is None:
         workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=w.device)
+    _bytes(workspace, "workspace", 0, torch.uint8)
     _check("fit_lut2", _lib.fit_lut2(_ptr(w), n, k, _ptr(idx), _ptr(centroids), _ptr(workspace),
                                      workspace.numel(), _stream(stream)))
     return idx, centroids
+
+
+# Bytes of the canonical (codes, scales or codebook) inputs of repack_weights.
+_CANONICAL_BYTES = {
+    QL_NVFP4: lambda n, k: (n * (k // 2), n * (k // 16)),
+    QL_INT4_G128: lambda n, k: (n * (k // 2), n * (k // 128) * 2),
+    QL_INT4_SP24: lambda n, k: (n * (k // 2), n * (k // 128) * 2),
+    QL_LUT2: lambda n, k: (n * (k // 4), n * 8),
+}
 
 
 def repack_weights_bytes(fmt, n, k):
@@ -170,9 +207,19 @@ def repack_weights_bytes(fmt, n, k):
 def repack_weights(fmt, n, k, codes, scales_or_lut, tensor_scale=None, packed=None, stream=None):
     """Repack canonical quantized weights into the kernel operand order.
     Returns the packed blob (uint8 GPU tensor)."""
+    if fmt not in _CANONICAL_BYTES:
+        raise ValueError(f"unknown weight format {fmt}")
+    code_bytes, aux_bytes = _CANONICAL_BYTES[fmt](n, k)
+    _bytes(codes, "codes", code_bytes, torch.uint8)
+    _bytes(scales_or_lut, "scales_or_lut", aux_bytes)
+    if fmt == QL_NVFP4:
+        if tensor_scale is None:
+            raise ValueError("an NVFP4 blob needs the weights' tensor_scale")
+        _bytes(tensor_scale, "tensor_scale", 4, torch.float32)
     nbytes = _lib.repack_weights_bytes(fmt, n, k)
     if packed is None:
         packed = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _bytes(packed, "packed", nbytes, torch.uint8)
     _check("repack_weights", _lib.repack_weights(
         fmt, n, k, _ptr(codes), _ptr(scales_or_lut), _ptr(tensor_scale), _ptr(packed),
         packed.numel(), _stream(stream)))

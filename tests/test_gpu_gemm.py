@@ -468,6 +468,30 @@ def test_binding_rejects_undersized_buffers():
         lambda: q.gemm_lut2(xb, i4[:1024], n, k),
         lambda: q.gemm_w4a16_sp24(xb.float(), i4, n, k),                   # fp32 activations
     ]
+    # weight preparation and the quantizer: short outputs, wrong input dtype,
+    # short canonical inputs of the repacker
+    wd = dev_f32(w)
+    wc, ws_, wt = q.quantize_nvfp4(wd)
+    c4, s4 = q.quantize_int4_g128(wd)
+    u8 = lambda nb: torch.empty(nb, dtype=torch.uint8, device="cuda")
+    bad += [
+        lambda: q.quantize_nvfp4(wd, codes=u8(n * k // 2 - 16)),
+        lambda: q.quantize_nvfp4(wd, scales=u8(n * k // 16 - 16)),
+        lambda: q.quantize_nvfp4(wd, ts_out=torch.empty(1, dtype=torch.float64, device="cuda")),
+        lambda: q.quantize_nvfp4(wd.reshape(1, n, k)),
+        lambda: q.quantize_int4_g128(wd.to(torch.bfloat16)),                 # bf16 read as fp32
+        lambda: q.quantize_int4_g128(wd, codes=u8(n * k // 2 - 16)),
+        lambda: q.quantize_int4_g128(wd, scales=u8(n * (k // 128) * 2 - 2)),
+        lambda: q.fit_lut2(wd.to(torch.bfloat16)),
+        lambda: q.fit_lut2(wd, idx=u8(n * k // 4 - 16)),
+        lambda: q.repack_weights(q.QL_NVFP4, n, k, wc[:-1], ws_, wt),
+        lambda: q.repack_weights(q.QL_NVFP4, n, k, wc, ws_[:-1], wt),
+        lambda: q.repack_weights(q.QL_NVFP4, n, k, wc, ws_, None),
+        lambda: q.repack_weights(q.QL_INT4_G128, n, k, c4, s4[:-1]),
+        lambda: q.repack_weights(q.QL_LUT2, n, k, c4[: n // 4], s4),           # idx rows missing
+        lambda: q.repack_weights(q.QL_INT4_G128, n, k, c4, s4, packed=u8(1024)),
+        lambda: q.repack_weights(7, n, k, c4, s4),
+    ]
     for fn in bad:
         with pytest.raises(ValueError):
             fn()
