@@ -292,9 +292,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
   }
 }
 
-// Sum of the k slices of one split tile (block = tail slot), in slice order
-// (deterministic), times the tensor scales, stored like the main epilogue.
-template <int WAVES, bool kBF16Out>
+// Sum of the k slices of the split tiles, in slice order (deterministic),
+// times the tensor scales, stored like the main epilogue.  Block = (tail
+// slot, 16-column strip i of each wave's 128 columns), so the reduction
+// spreads over tail * 8 blocks; each thread loads all MAXS slices of its four
+// accumulators before adding (slice indices past `splits` re-read the last
+// slice and are not added), so one memory round trip serves the whole sum.
+template <int WAVES, int MAXS, bool kBF16Out>
 __global__ __launch_bounds__(WAVES * 64) void w4a4_split_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ a_ts,
     const uint8_t* __restrict__ blob, int M, int N, int K, int full, int splits,
@@ -302,35 +306,56 @@ __global__ __launch_bounds__(WAVES * 64) void w4a4_split_reduce_kernel(
   if (!blob_matches(blob, 0, N, K)) return;
   constexpr int WGM = WAVES / 2, TN = 8, TM = BM / WGM / 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = blockIdx.x;
+  const int slot = blockIdx.x / TN, i = blockIdx.x % TN;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int m0, n0;
   coop_tile_origin(full + slot, tiles_m, tiles_n, m0, n0);
-  const float stv = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
   const floatx4* src = reinterpret_cast<const floatx4*>(part) +
-                       (int64_t(slot * splits) * WAVES + wave) * (TN * TM * 64) + lane;
+                       (int64_t(slot * splits) * WAVES + wave) * (TN * TM * 64) + i * TM * 64 +
+                       lane;
   const int64_t slice_stride = int64_t(WAVES) * TN * TM * 64;
+  floatx4 v[MAXS][TM];
+#pragma unroll
+  for (int sl = 0; sl < MAXS; ++sl)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) v[sl][j] = src[min(sl, splits - 1) * slice_stride + j * 64];
+  const float stv = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
   const int wn = wave & 1, wm = wave >> 1;
   const int r = lane & 15, q = lane >> 4;
-  for (int i = 0; i < TN; ++i) {
-    const int n = n0 + wn * 128 + i * 16 + 4 * q;
+  const int n = n0 + wn * 128 + i * 16 + 4 * q;
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      floatx4 a = src[(i * TM + j) * 64];
-      for (int sl = 1; sl < splits; ++sl) a += src[sl * slice_stride + (i * TM + j) * 64];
-      const int m = m0 + wm * (TM * 16) + j * 16 + r;
-      if (n >= N || m >= M) continue;
-      const floatx4 v = a * stv;
-      if (kBF16Out) {
-        uint2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
-      } else {
-        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
-      }
+  for (int j = 0; j < TM; ++j) {
+    floatx4 a = v[0][j];
+#pragma unroll
+    for (int sl = 1; sl < MAXS; ++sl)
+      if (sl < splits) a += v[sl][j];
+    const int m = m0 + wm * (TM * 16) + j * 16 + r;
+    if (n >= N || m >= M) continue;
+    const floatx4 o = a * stv;
+    if (kBF16Out) {
+      uint2 h;
+      h.x = pack_bf16x2(o[0], o[1]);
+      h.y = pack_bf16x2(o[2], o[3]);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = h;
+    } else {
+      *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = o;
     }
   }
+}
+
+template <int WAVES, bool kBF16Out>
+void launch_split_reduce(const float* part, const float* a_ts, const uint8_t* blob, int64_t m,
+                         int64_t n, int64_t k, void* y, const CoopSplit& P, hipStream_t s) {
+  const dim3 grid(P.tail * 8), block(WAVES * 64);
+  if (P.splits <= 2)
+    w4a4_split_reduce_kernel<WAVES, 2, kBF16Out><<<grid, block, 0, s>>>(
+        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
+  else if (P.splits <= 4)
+    w4a4_split_reduce_kernel<WAVES, 4, kBF16Out><<<grid, block, 0, s>>>(
+        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
+  else
+    w4a4_split_reduce_kernel<WAVES, 8, kBF16Out><<<grid, block, 0, s>>>(
+        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
 }
 
 template <int WAVES, int RS>
@@ -360,11 +385,9 @@ hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const fl
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.tail == 0) return e;
   if (y_dtype == 1)
-    w4a4_split_reduce_kernel<WAVES, true><<<P.tail, WAVES * 64, 0, s>>>(
-        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
+    launch_split_reduce<WAVES, true>(part, a_ts, blob, m, n, k, y, P, s);
   else
-    w4a4_split_reduce_kernel<WAVES, false><<<P.tail, WAVES * 64, 0, s>>>(
-        part, a_ts, blob, int(m), int(n), int(k), P.full, P.splits, y);
+    launch_split_reduce<WAVES, false>(part, a_ts, blob, m, n, k, y, P, s);
   return hipGetLastError();
 }
 
