@@ -366,6 +366,8 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
     (4096, 5120, 17408),  # 27B-class down at M = 4096 (the benchmarked split shapes)
     (4347, 4096, 2048),   # 17 x 16 tiles, ragged M
     (4352, 4096, 256),    # K = 256: two stage pairs, so at most two slices
+    (4096, 5376, 1024),   # 336 tiles: 80 in the last round, 3 slices
+    (4096, 4864, 1024),   # 304 tiles: 48 in the last round, 5 slices
 ])
 def test_w4a4_split_last_round(m, n, k):
     q = require_gpu()
