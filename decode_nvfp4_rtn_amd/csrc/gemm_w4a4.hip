@@ -261,19 +261,31 @@ hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 namespace {
 
 // The block-cooperative 256x256 kernel holds one block per CU (its LDS double
-// buffer is 160 KiB), so it needs at least one tile per CU; smaller problems
-// take the 128x128 per-wave kernel, which spreads 4x more blocks.  It also
-// addresses activation and weight codes with 31-bit buffer offsets.
+// buffer is 160 KiB).  It runs every problem of more than half a round of
+// 256x256 tiles (more than CUs / 2 tiles); a problem of at most half a round
+// runs on it only when the caller's workspace lets its tiles be split along k
+// over the CUs, and otherwise takes the 128x128 per-wave kernel, which
+// spreads 4x more blocks.  Measured on Qwen3-8B-like and 27B-class shapes at
+// M = 512-3072: 129-255 tiles on the cooperative kernel run 1.21-1.45x the
+// per-wave kernel's speed; the split of a small problem 1.00-2.18x (most on
+// long k).  The kernel addresses activation and weight codes with 31-bit
+// buffer offsets.
+bool coop_fits(int64_t m, int64_t n, int64_t k) {
+  const int64_t lim = (int64_t(1) << 31) - (int64_t(1) << 20);
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  return m * (k / 2) <= lim && n * (k / 2) <= lim && big_tiles < (int64_t(1) << 30);
+}
+
 bool use_coop(int64_t m, int64_t n, int64_t k) {
   const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  const int64_t lim = (int64_t(1) << 31) - (int64_t(1) << 20);
-  return big_tiles >= 256 && m * (k / 2) <= lim && n * (k / 2) <= lim;
+  const int cus = device_cu_count();
+  return (cus > 0 ? big_tiles * 2 > cus : big_tiles >= 256) && coop_fits(m, n, k);
 }
 
 }  // namespace
 
 size_t gemm_w4a4_ws_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m <= 0 || n <= 0 || k <= 0 || !use_coop(m, n, k)) return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || !coop_fits(m, n, k)) return 0;
   return coop_split_bytes(coop_split_plan(m, n, k));
 }
 
@@ -282,12 +294,11 @@ hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, con
                             int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {
   const BlobLayout L = blob_layout(0, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
-  if (use_coop(m, n, k)) {
-    const size_t need = coop_split_bytes(coop_split_plan(m, n, k));
-    const bool split = need > 0 && ws != nullptr && ws_bytes >= need;
+  const size_t need = coop_fits(m, n, k) ? coop_split_bytes(coop_split_plan(m, n, k)) : 0;
+  const bool split = need > 0 && ws != nullptr && ws_bytes >= need;
+  if (split || use_coop(m, n, k))
     return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype,
                                  static_cast<float*>(ws), split, s);
-  }
   return launch_tile<4, 4>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
 }
 

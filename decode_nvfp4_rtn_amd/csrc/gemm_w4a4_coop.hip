@@ -393,18 +393,18 @@ hipError_t launch_coop(const uint8_t* a_codes, const uint8_t* a_scales, const fl
 
 }  // namespace
 
-// Tiles are dispatched in rounds of one per CU.  When the last round is at
-// most half full, its tiles are split along k into `splits` slices (pairs of
-// stages, at most 8 slices) so that the round occupies the CUs; the slices'
-// fp32 partial tiles are summed by a second launch.  Measured on the
-// 27B-class layers at M = 4096: o_proj (5120 x 5120, 1.25 rounds) 863 -> 992
-// TFLOP/s, down (5120 x 17408, 1.25 rounds) 943 -> 1279, gate_up (8.5
-// rounds) +2 %.
+// Tiles are dispatched in rounds of one per CU.  When the last round (or a
+// problem of less than one round) is at most half full, its tiles are split
+// along k into `splits` slices (pairs of stages, at most 8 slices) so that
+// the round occupies the CUs; the slices' fp32 partial tiles are summed by a
+// second launch.  Measured on the 27B-class layers at M = 4096: o_proj
+// (5120 x 5120, 1.25 rounds) 863 -> 992 TFLOP/s, down (5120 x 17408, 1.25
+// rounds) 943 -> 1279, gate_up (8.5 rounds) +2 %.
 CoopSplit coop_split_plan(int64_t m, int64_t n, int64_t k) {
   const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
   const int cus = device_cu_count();
   CoopSplit P{tiles, 0, 1};
-  if (cus <= 0 || tiles <= cus) return P;
+  if (cus <= 0) return P;
   const int tail = tiles % cus;
   if (tail == 0) return P;
   int splits = cus / tail;

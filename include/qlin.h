@@ -199,18 +199,20 @@ int gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales,
 /* ------------------------------------------------------------------------
  * gemm_w4a4 with a caller-provided workspace that lets the last, partly
  * filled round of 256 x 256 output tiles (one tile per compute unit and
- * round) be split along k over the idle compute units: fp32 partial tiles go
- * to the workspace and a second launch adds them in a fixed order (so
- * results stay deterministic; they differ from gemm_w4a4's in fp32 rounding
- * only).  Same arithmetic definition and arguments as gemm_w4a4, plus:
+ * round), or a whole problem of at most half a round, be split along k over
+ * the idle compute units: fp32 partial tiles go to the workspace and a
+ * second launch adds them in a fixed order (so results stay deterministic;
+ * they differ from gemm_w4a4's in fp32 rounding only).  Same arithmetic
+ * definition and arguments as gemm_w4a4, plus:
  *
  * workspace        device memory of at least gemm_w4a4_workspace(m, n, k)
  *                  bytes, 16-byte aligned, not read before it is written;
  *                  may be NULL (then the call is gemm_w4a4).  Calls that
  *                  share one workspace must be ordered (same stream).
  * gemm_w4a4_workspace returns 0 when no split applies to the shape (the
- * tiles fill whole rounds, or the last round is more than half full), and
- * depends on the current device's compute-unit count.
+ * tiles fill whole rounds, the last round is more than half full, or k is
+ * too short for two slices), and depends on the current device's
+ * compute-unit count.
  * Errors: as gemm_w4a4, and QL_EWORKSPACE when workspace is non-NULL and
  * smaller than gemm_w4a4_workspace(m, n, k).
  * ---------------------------------------------------------------------- */

@@ -326,15 +326,19 @@ def test_decode_persistent_tile_walk(fmt, n, k):
 
 
 # ------------------------------------------ cooperative W4A4, ragged edges --
-# Problems with at least 256 tiles of 256 x 256 take the block-cooperative
-# kernel.  With M and N not multiples of 256 its edge blocks read clamped
-# (last valid) rows for the rows past M or N; those products must reach no
-# stored output.  Checked on the last rows and columns and a sample.
+# Problems of more than half a round of 256 x 256 tiles (more tiles than
+# CUs / 2) take the block-cooperative kernel.  With M and N not multiples of
+# 256 its edge blocks read clamped (last valid) rows for the rows past M or
+# N; those products must reach no stored output.  Checked on the last rows
+# and columns and a sample.
 
-@pytest.mark.parametrize("m,n,k", [(4100, 16400, 512), (8191, 8208, 640)])
+@pytest.mark.parametrize("m,n,k", [(4100, 16400, 512), (8191, 8208, 640),
+                                   (2100, 4000, 640),    # 144 tiles: less than one round
+                                   (2048, 6144, 1024)])  # 192 tiles
 def test_w4a4_cooperative_ragged_edges(m, n, k):
     q = require_gpu()
-    assert ((m + 255) // 256) * ((n + 255) // 256) >= 256
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 2 * ((m + 255) // 256) * ((n + 255) // 256) > cus
     bits = synth.activations_bf16(11, m, m, k, outliers="channels")
     w = synth.weights(11, n, n, k)
     say("w4a4 coop ragged", m, n, k)
@@ -355,8 +359,9 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
 
 
 # ------------------------------ cooperative W4A4, k split of the last round --
-# With a workspace, a last round of tiles that is at most half full is split
-# along k over the idle CUs (fp32 partial tiles, then a fixed-order sum).  The
+# With a workspace, a last round of tiles that is at most half full, or a
+# whole problem of at most half a round, is split along k over the idle CUs
+# (fp32 partial tiles, then a fixed-order sum).  The
 # oracle checks a sample; the whole output is compared with the unsplit call
 # (already pinned to the oracle by the tests above), which differs only in the
 # fp32 summation order.
@@ -368,6 +373,9 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
     (4352, 4096, 256),    # K = 256: two stage pairs, so at most two slices
     (4096, 5376, 1024),   # 336 tiles: 80 in the last round, 3 slices
     (4096, 4864, 1024),   # 304 tiles: 48 in the last round, 5 slices
+    (1024, 5120, 17408),  # 80 tiles, less than one round: 3 slices
+    (300, 4096, 1024),    # 32 tiles, ragged M: 8 slices
+    (64, 256, 512),       # a single tile: 4 slices (two stages each)
 ])
 def test_w4a4_split_last_round(m, n, k):
     q = require_gpu()
@@ -376,7 +384,7 @@ def test_w4a4_split_last_round(m, n, k):
     tail = tiles % cus
     need = q.gemm_w4a4_workspace(m, n, k)
     splits = min(cus // tail, k // 128, 8) if 0 < tail else 0
-    if not (tiles > cus and splits >= 2):
+    if splits < 2:
         pytest.skip(f"{tiles} tiles on {cus} CUs: no split applies")
     assert need == tail * splits * 256 * 256 * 4
     bits = synth.activations_bf16(12, m, m, k, outliers="channels")
@@ -405,9 +413,14 @@ def test_w4a4_split_last_round(m, n, k):
 def test_w4a4_workspace_not_needed_for_whole_rounds():
     q = require_gpu()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    # whole rounds of tiles on this device, and a small problem (per-wave kernel)
+    # whole rounds of tiles on this device, a last round more than half full,
+    # a problem of more than half a round, and k too short for two slices
     assert q.gemm_w4a4_workspace(256 * cus, 256, 512) == 0
-    assert q.gemm_w4a4_workspace(64, 256, 512) == 0
+    assert q.gemm_w4a4_workspace(256 * (cus + cus // 2 + 1), 256, 512) == 0
+    assert q.gemm_w4a4_workspace(256 * (cus // 2 + 1), 256, 512) == 0
+    assert q.gemm_w4a4_workspace(64, 256, 128) == 0
+    # a small problem with room for slices needs one
+    assert q.gemm_w4a4_workspace(64, 256, 512) == 4 * 256 * 256 * 4
 
 
 # ------------------------------------------------------------ blob guard --
