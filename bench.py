@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--no-bf16-reference", action="store_true")
     ap.add_argument("--no-27b", action="store_true",
                     help="skip the 27B-class prefill measurement (M = 4096, 16384, 32768)")
+    ap.add_argument("--no-small-m", action="store_true",
+                    help="skip the smaller prefill batches (M = 512 / 1024 / 2048)")
     ap.add_argument("--no-odp", action="store_true",
                     help="skip the host-to-device weight streaming measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -456,6 +458,56 @@ def main():
         del R
         torch.cuda.empty_cache()
 
+    # ------------------------------------------ smaller prefill batches ----
+    # The Qwen3-8B-like layers at M = 512 / 1024 / 2048 (the first M rows of
+    # the same inputs), quantize + GEMM, with a gemm_w4a4 workspace where a k
+    # split applies.  With fewer 256 x 256 tiles than CUs these show the
+    # GEMM's dispatch: the cooperative kernel above half a round of tiles,
+    # its k split below that (workspace), never the per-wave kernel here.
+    small = {}
+    if not args.no_small_m:
+        SM = (512, 1024, 2048)
+        gws = {}
+        for i, p in enumerate(P):
+            for m in SM:
+                nb = qlin.gemm_w4a4_workspace(m, p["L"].n, p["L"].k)
+                gws[(m, i)] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        tq = {(m, i): [] for m in SM for i in range(len(P))}
+        tg = {(m, i): [] for m in SM for i in range(len(P))}
+        for rep in range(6):
+            for m in SM:
+                for i, p in enumerate(P):
+                    L = p["L"]
+                    e0, e1, e2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
+                    e0.record()
+                    qlin.quantize_nvfp4(p["x"][:m], codes=p["codes"][:m], scales=p["scales"][:m],
+                                        workspace=p["ws"], ts_out=p["ts"])
+                    e1.record()
+                    qlin.gemm_w4a4(p["codes"][:m], p["scales"][:m], p["ts"], p["blob"], m, L.n, L.k,
+                                   y=p["y"][:m], workspace=gws[(m, i)])
+                    e2.record()
+                    if rep > 0:   # the first round is a warm-up
+                        tq[(m, i)].append((e0, e1))
+                        tg[(m, i)].append((e1, e2))
+        torch.cuda.synchronize()
+        for m in SM:
+            rows, fl_all, q_all, g_all = [], 0.0, 0.0, 0.0
+            for i, p in enumerate(P):
+                L = p["L"]
+                q = float(np.median([a.elapsed_time(b) for a, b in tq[(m, i)]]))
+                g = float(np.median([a.elapsed_time(b) for a, b in tg[(m, i)]]))
+                fl = 2.0 * m * L.n * L.k
+                fl_all, q_all, g_all = fl_all + fl, q_all + q, g_all + g
+                nb = 0 if gws[(m, i)] is None else gws[(m, i)].numel()
+                rows.append({"layer": L.name, "gemm_us": round(g * 1e3, 1),
+                             "gemm_tflops": round(fl / g / 1e9, 1), "quantize_us": round(q * 1e3, 1),
+                             "k_split_workspace_mb": round(nb / 1e6, 1)})
+            small[f"m{m}"] = {"layers": rows, "gemm_tflops": round(fl_all / g_all / 1e9, 1),
+                              "prefill_tflops_incl_quantize": round(fl_all / (g_all + q_all) / 1e9, 1)}
+            _progress(f"small m={m}: GEMM {small[f'm{m}']['gemm_tflops']} TFLOP/s")
+        small["activations"] = "first M rows of the M = 8192 inputs; median of 5 interleaved rounds"
+        del gws
+
     # ------------------------------------------- BF16 reference points ----
     # The pages state their speed-ups against BF16; torch's bf16 matmul
     # (hipBLASLt) on the same shapes is that reference here: prefill
@@ -574,6 +626,7 @@ def main():
             "bf16_reference": bf16_ref,
             "odp_weight_streaming": odp,
             "prefill_27b": big,
+            "prefill_small_m": small,
             "w4a4_gemm_speedup_vs_bf16": (
                 round(sum(v["us"] for k, v in bf16_ref.items() if k.startswith("prefill/"))
                       / (gemm_ms_step * 1e3), 3) if bf16_ref else None),
