@@ -63,7 +63,11 @@ def test_w4a4_tiny_full():
     _check(host_f64(y), ref, False)
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 48, 256), (130, 272, 384), (257, 128, 1024)])
+# Small problems without a workspace take the per-wave kernel: 64 x 64 tiles
+# while there are fewer 128 x 128 tiles than CUs, 128 x 128 tiles above that
+# (the last shape: 264 of them, ragged in M and N).
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 48, 256), (130, 272, 384), (257, 128, 1024),
+                                   (1000, 4112, 640)])
 def test_w4a4_ragged(m, n, k):
     q = require_gpu()
     x = synth.activations(8, m, m, k, outliers="channels")
