@@ -282,11 +282,28 @@ bool use_coop(int64_t m, int64_t n, int64_t k) {
   return (cus > 0 ? big_tiles * 2 > cus : big_tiles >= 256) && coop_fits(m, n, k);
 }
 
+// A problem of at most half a round is k-split only where that beats the
+// per-wave kernel: not at m <= 128 (half of each 256-row tile would be idle
+// MFMA work) unless k is long.  Measured over the Qwen3-8B-like and 27B-class
+// shapes at m = 128-2048: the split ran 0.80-0.99x at m = 128 with k <= 5120,
+// 1.47-1.58x there with k >= 12288, and 0.93-1.99x (mostly > 1) at m >= 256.
+bool split_pays(int64_t m, int64_t n, int64_t k) {
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  const int cus = device_cu_count();
+  if (cus > 0 && big_tiles * 2 <= cus) return m > 128 || k >= 8192;
+  return true;
+}
+
+size_t split_bytes(int64_t m, int64_t n, int64_t k) {
+  if (!coop_fits(m, n, k) || !split_pays(m, n, k)) return 0;
+  return coop_split_bytes(coop_split_plan(m, n, k));
+}
+
 }  // namespace
 
 size_t gemm_w4a4_ws_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m <= 0 || n <= 0 || k <= 0 || !coop_fits(m, n, k)) return 0;
-  return coop_split_bytes(coop_split_plan(m, n, k));
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  return split_bytes(m, n, k);
 }
 
 hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
@@ -294,7 +311,7 @@ hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, con
                             int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {
   const BlobLayout L = blob_layout(0, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
-  const size_t need = coop_fits(m, n, k) ? coop_split_bytes(coop_split_plan(m, n, k)) : 0;
+  const size_t need = split_bytes(m, n, k);
   const bool split = need > 0 && ws != nullptr && ws_bytes >= need;
   if (split || use_coop(m, n, k))
     return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype,

@@ -379,7 +379,7 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
     (4096, 4864, 1024),   # 304 tiles: 48 in the last round, 5 slices
     (1024, 5120, 17408),  # 80 tiles, less than one round: 3 slices
     (300, 4096, 1024),    # 32 tiles, ragged M: 8 slices
-    (64, 256, 512),       # a single tile: 4 slices (two stages each)
+    (64, 256, 8192),      # a single tile, M <= 128 with long k: 8 slices
 ])
 def test_w4a4_split_last_round(m, n, k):
     q = require_gpu()
@@ -388,6 +388,8 @@ def test_w4a4_split_last_round(m, n, k):
     tail = tiles % cus
     need = q.gemm_w4a4_workspace(m, n, k)
     splits = min(cus // tail, k // 128, 8) if 0 < tail else 0
+    if 2 * tiles <= cus and m <= 128 and k < 8192:
+        splits = 0   # the per-wave kernel is faster there
     if splits < 2:
         pytest.skip(f"{tiles} tiles on {cus} CUs: no split applies")
     assert need == tail * splits * 256 * 256 * 4
@@ -423,8 +425,11 @@ def test_w4a4_workspace_not_needed_for_whole_rounds():
     assert q.gemm_w4a4_workspace(256 * (cus + cus // 2 + 1), 256, 512) == 0
     assert q.gemm_w4a4_workspace(256 * (cus // 2 + 1), 256, 512) == 0
     assert q.gemm_w4a4_workspace(64, 256, 128) == 0
+    # M <= 128 with short k: the per-wave kernel, no split
+    assert q.gemm_w4a4_workspace(64, 256, 512) == 0
     # a small problem with room for slices needs one
-    assert q.gemm_w4a4_workspace(64, 256, 512) == 4 * 256 * 256 * 4
+    assert q.gemm_w4a4_workspace(256, 256, 512) == 4 * 256 * 256 * 4
+    assert q.gemm_w4a4_workspace(64, 256, 8192) == 8 * 256 * 256 * 4
 
 
 # ------------------------------------------------------------ blob guard --
