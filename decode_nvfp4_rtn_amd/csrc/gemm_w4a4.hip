@@ -262,7 +262,7 @@ namespace {
 
 // The block-cooperative 256x256 kernel holds one block per CU (its LDS double
 // buffer is 160 KiB).  It runs every problem of more than half a round of
-// 256x256 tiles (more than CUs / 2 tiles); a problem of at most half a round
+// 256x256 tiles (more than CUs / 2 tiles) with m > 128; a problem of at most half a round
 // runs on it only when the caller's workspace lets its tiles be split along k
 // over the CUs, and otherwise takes the 128x128 per-wave kernel, which
 // spreads 4x more blocks.  Measured on Qwen3-8B-like and 27B-class shapes at
@@ -276,10 +276,13 @@ bool coop_fits(int64_t m, int64_t n, int64_t k) {
   return m * (k / 2) <= lim && n * (k / 2) <= lim && big_tiles < (int64_t(1) << 30);
 }
 
+// At m <= 128 half of each 256-row tile would be idle MFMA work: the
+// per-wave kernel's 128-row tiles measured 1.24-1.54x faster there (n =
+// 40960-151936, k = 4096, bit-identical outputs).
 bool use_coop(int64_t m, int64_t n, int64_t k) {
   const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
   const int cus = device_cu_count();
-  return (cus > 0 ? big_tiles * 2 > cus : big_tiles >= 256) && coop_fits(m, n, k);
+  return m > 128 && (cus > 0 ? big_tiles * 2 > cus : big_tiles >= 256) && coop_fits(m, n, k);
 }
 
 // A problem of at most half a round is k-split only where that beats the
@@ -291,7 +294,7 @@ bool split_pays(int64_t m, int64_t n, int64_t k) {
   const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
   const int cus = device_cu_count();
   if (cus > 0 && big_tiles * 2 <= cus) return m > 128 || k >= 8192;
-  return true;
+  return m > 128;   // larger problems at m <= 128 take the per-wave kernel
 }
 
 size_t split_bytes(int64_t m, int64_t n, int64_t k) {

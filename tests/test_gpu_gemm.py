@@ -65,9 +65,10 @@ def test_w4a4_tiny_full():
 
 # Small problems without a workspace take the per-wave kernel: 64 x 64 tiles
 # while there are fewer 128 x 128 tiles than CUs, 128 x 128 tiles above that
-# (the last shape: 264 of them, ragged in M and N).
+# (1000 x 4112: 264 of them, ragged in M and N).  So does M <= 128 at any N
+# (96 x 40976: 161 tiles of 256 x 256, ragged N).
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 48, 256), (130, 272, 384), (257, 128, 1024),
-                                   (1000, 4112, 640)])
+                                   (1000, 4112, 640), (96, 40976, 256)])
 def test_w4a4_ragged(m, n, k):
     q = require_gpu()
     x = synth.activations(8, m, m, k, outliers="channels")
@@ -388,7 +389,7 @@ def test_w4a4_split_last_round(m, n, k):
     tail = tiles % cus
     need = q.gemm_w4a4_workspace(m, n, k)
     splits = min(cus // tail, k // 128, 8) if 0 < tail else 0
-    if 2 * tiles <= cus and m <= 128 and k < 8192:
+    if m <= 128 and not (2 * tiles <= cus and k >= 8192):
         splits = 0   # the per-wave kernel is faster there
     if splits < 2:
         pytest.skip(f"{tiles} tiles on {cus} CUs: no split applies")
@@ -425,8 +426,9 @@ def test_w4a4_workspace_not_needed_for_whole_rounds():
     assert q.gemm_w4a4_workspace(256 * (cus + cus // 2 + 1), 256, 512) == 0
     assert q.gemm_w4a4_workspace(256 * (cus // 2 + 1), 256, 512) == 0
     assert q.gemm_w4a4_workspace(64, 256, 128) == 0
-    # M <= 128 with short k: the per-wave kernel, no split
+    # M <= 128 with short k, or above half a round: the per-wave kernel, no split
     assert q.gemm_w4a4_workspace(64, 256, 512) == 0
+    assert q.gemm_w4a4_workspace(128, 256 * (cus + cus // 4), 512) == 0
     # a small problem with room for slices needs one
     assert q.gemm_w4a4_workspace(256, 256, 512) == 4 * 256 * 256 * 4
     assert q.gemm_w4a4_workspace(64, 256, 8192) == 8 * 256 * 256 * 4
