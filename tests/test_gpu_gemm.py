@@ -205,6 +205,24 @@ def test_w4a16_ragged_batches(m):
     _check(host_f64(y), gemm.w4a16(xb, *int4.quantize(w)), False)
 
 
+# Long K with one row tile per block: the pipelined k-split kernel at M <= 16
+# (an odd number of chunks, waves whose last chunk is clamped), the k-split
+# kernel with two m-tiles above (ragged second m-tile).
+@pytest.mark.parametrize("m,k", [(17, 10240), (25, 8576), (32, 10240), (9, 8576)])
+def test_w4a16_pipelined_long_k(m, k):
+    q = require_gpu()
+    n = 272
+    w = synth.weights(9, 1, n, k)
+    xb = synth.activations_bf16(9, 2, m, k)
+    say("w4a16 pipelined long k", m, k)
+    blob = _int4_blob(q, w)
+    ref = gemm.w4a16(xb, *int4.quantize(w))
+    for dt in (torch.float32, torch.bfloat16):
+        y = q.gemm_w4a16(dev_bf16(xb), blob, n, k, out_dtype=dt)
+        torch.cuda.synchronize()
+        _check(host_f64(y), ref, dt == torch.bfloat16)
+
+
 def test_w4a16_one_hot_layout_probe():
     q = require_gpu()
     n, k = 48, 384
