@@ -53,6 +53,9 @@ class PrefillWeightStream:
         self.copy_stream = torch.cuda.Stream(device=self.device)
         self.ready = [torch.cuda.Event() for _ in range(2)]
         self.free = [torch.cuda.Event() for _ in range(2)]
+        # free[b] has been recorded after the last GEMMs that read buffer b,
+        # by this run() or an earlier one; a later copy into b must wait on it
+        self.recorded = [False, False]
 
     def _blob(self, buf, blk, j):
         o = self.offsets[blk][j]
@@ -61,8 +64,9 @@ class PrefillWeightStream:
     def _issue_copy(self, step, blk):
         b = step % 2
         with torch.cuda.stream(self.copy_stream):
-            if step >= 2:
-                # buffer b still holds block step-2 until its last GEMM has run
+            if self.recorded[b]:
+                # buffer b holds the block of an earlier step (of this run or of
+                # an earlier run) until the GEMMs that read it have run
                 self.copy_stream.wait_event(self.free[b])
             for j, h in enumerate(self.host_blocks[blk]):
                 self._blob(b, blk, j).copy_(h, non_blocking=True)
@@ -75,7 +79,9 @@ class PrefillWeightStream:
         block's streamed weights into ys[j]; shapes[j] = (n, k).  codes,
         scales, tscales and workspaces are the per-layer quantizer outputs and
         workspace (see qlin.quantize_nvfp4).  Work is enqueued on the current
-        stream (compute) and the copy stream; nothing synchronises the host.
+        stream (compute) and the copy stream; nothing synchronises the host,
+        and back-to-back calls are ordered on the device: a copy into a buffer
+        waits for the GEMMs of any earlier call that read that buffer.
         """
         compute = torch.cuda.current_stream(self.device)
         self._issue_copy(0, order[0])
@@ -91,4 +97,5 @@ class PrefillWeightStream:
                 qlin.gemm_w4a4(codes[j], scales[j], tscales[j], self._blob(b, blk, j),
                                xs[j].shape[0], n, k, y=ys[j])
             self.free[b].record(compute)
+            self.recorded[b] = True
         return ys

@@ -26,13 +26,24 @@ def say(*a):
     sys.stdout.flush()
 
 
+def _host(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a if a.flags.writeable else a.copy()   # torch wants writable host arrays
+
+
 def dev_f32(a):
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return torch.from_numpy(_host(a, np.float32)).cuda()
 
 
 def dev_bf16(bits):
     """uint16 bf16 bit patterns -> GPU bfloat16 tensor."""
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(_host(bits, np.uint16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def rows_f64(t, rows):
+    """Rows `rows` (numpy indices) of a GPU matrix, as float64 host values."""
+    sel = t.index_select(0, torch.from_numpy(np.asarray(rows, dtype=np.int64)).to(t.device))
+    return host_f64(sel)
 
 
 def host_u8(t):

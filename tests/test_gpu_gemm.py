@@ -3,9 +3,11 @@
 Bar: max |y - y_ref| / rms(y_ref) <= 1e-3 for fp32 outputs; for bf16 outputs
 the per-element rule of oracle.gemm.bf16_output_ok.  The oracle quantizes its
 own operands from the same seeded inputs (bit-equality of those codes with the
-GPU's is checked in test_gpu_quantize.py); at full size it computes the
-outputs of a seeded sample of rows and columns, one by one, in the launch
-configuration the benchmark times.
+GPU's is checked in test_gpu_quantize.py).  At full size it computes 1024
+seeded rows (always including the last) times every column of each W4A4
+output, and every output of the decode GEMMs, in the launch configuration
+the benchmark times (the same inputs, and the k-split workspace wherever the
+benchmark passes one).
 """
 
 import numpy as np
@@ -14,7 +16,9 @@ import torch
 
 from decode_nvfp4_rtn_amd import synth, configs
 from oracle import nvfp4, int4, lut2, gemm
-from tests.gpu_common import (require_gpu, say, dev_f32, dev_bf16, host_f64, sample_rows)
+from tests import oracle_rows as orows
+from tests.gpu_common import (require_gpu, say, dev_f32, dev_bf16, host_f64, host_u8, rows_f64,
+                              sample_rows)
 
 pytestmark = pytest.mark.gpu
 TOL = gemm.TOL
@@ -83,39 +87,67 @@ def test_w4a4_ragged(m, n, k):
         _check(host_f64(y), ref, dt == torch.bfloat16)
 
 
-def _w4a4_sampled(q, cfg, layer_idx, layer, m, outliers):
-    n, k = layer.n, layer.k
-    bits = synth.activations_bf16(cfg.cid, layer_idx, m, k, outliers=outliers)
-    w = synth.weights(cfg.cid, layer_idx, n, k)
-    say("w4a4 full", cfg.name, layer.name, m, n, k)
-    blob = _nvfp4_blob(q, w)
+# One prefill layer at a time: the oracle's quantization of its weights (every
+# row), its GPU blob, and the activations at the largest M of the case list
+# (smaller M are their first rows, as the seeded draw is by 256-row block).
+_LAYER = {}
+
+
+def _prefill_layer(q, cfg, li, m_max):
+    key = (cfg.cid, li)
+    if key not in _LAYER:
+        _LAYER.clear()
+        L = cfg.layers[li]
+        w = orows.weights(cfg.cid, li, L.n, L.k)
+        wq = orows.nvfp4_quantize(w, nvfp4.tensor_scale(w))
+        blob = _nvfp4_blob(q, w)
+        del w
+        bits = orows.activations_bf16(cfg.cid, li, m_max, L.k, outliers=cfg.outliers)
+        _LAYER[key] = dict(wq=wq, blob=blob, bits=bits)
+    return _LAYER[key]
+
+
+def _w4a4_full_size(q, cfg, li, m, m_max):
+    """quantize_nvfp4 + gemm_w4a4 on the benchmark's input of this layer and M
+    (with a k-split workspace when the shape has one, as the benchmark does);
+    1024 seeded rows x every column against the oracle."""
+    L = cfg.layers[li]
+    n, k = L.n, L.k
+    c = _prefill_layer(q, cfg, li, m_max)
+    bits = c["bits"][:m]
+    nb = q.gemm_w4a4_workspace(m, n, k)
+    say("w4a4 full", cfg.name, L.name, m, n, k, "workspace", nb)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
     ac, as_, at = q.quantize_nvfp4(dev_bf16(bits))
-    y32 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.float32)
-    y16 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16)
+    y32 = q.gemm_w4a4(ac, as_, at, c["blob"], m, n, k, out_dtype=torch.float32, workspace=ws)
+    y16 = q.gemm_w4a4(ac, as_, at, c["blob"], m, n, k, out_dtype=torch.bfloat16, workspace=ws)
     torch.cuda.synchronize()
-    rows = sample_rows(m, 48, 7 * m + n)
-    cols = sample_rows(n, 48, 11 * n + k)
-    xf = synth.bf16_bits_as_f32(bits)
+    rows = sample_rows(m, 1024, 7 * m + n)
+    g32, g16 = rows_f64(y32, rows), rows_f64(y16, rows)
+    gcodes = host_u8(ac.index_select(0, torch.from_numpy(rows).cuda()))
+    del y32, y16, ac, as_, ws
+    xf = orows.bf16_as_f32(bits)
     st_a = nvfp4.tensor_scale(xf)
-    st_w = nvfp4.tensor_scale(w)
-    ref = gemm.w4a4(*nvfp4.quantize(xf[rows], s_t=st_a), *nvfp4.quantize(w[cols], s_t=st_w))
-    _check(host_f64(y32)[np.ix_(rows, cols)], ref, False)
-    _check(host_f64(y16)[np.ix_(rows, cols)], ref, True)
+    assert np.float32(at.item()) == st_a
+    aq = nvfp4.quantize(xf[rows], s_t=st_a)
+    assert np.array_equal(gcodes, aq[0])
+    ref = gemm.w4a4(*aq, *c["wq"])
+    _check(g32, ref, False)
+    _check(g16, ref, True)
 
 
 @pytest.mark.parametrize("li", range(4))
 def test_w4a4_qwen3_prefill_full_size(li):
     q = require_gpu()
-    cfg = configs.QWEN3_PREFILL
-    _w4a4_sampled(q, cfg, li, cfg.layers[li], 8192, cfg.outliers)
+    _w4a4_full_size(q, configs.QWEN3_PREFILL, li, 8192, 8192)
 
 
-@pytest.mark.parametrize("li,m", [(0, 4096), (1, 4096), (2, 4096), (3, 4096), (0, 32768),
-                                  (3, 16384)])
+# All twelve (layer, M) cases of the 27B-class set, layer by layer.
+@pytest.mark.parametrize("li,m", [(li, m) for li in range(4) for m in (4096, 16384, 32768)])
 def test_w4a4_27b_prefill_full_size(li, m):
     q = require_gpu()
     cfg = configs.BIG27_PREFILL
-    _w4a4_sampled(q, cfg, li, cfg.layers[li], m, cfg.outliers)
+    _w4a4_full_size(q, cfg, li, m, max(cfg.ms))
 
 
 def test_w4a4_one_hot_layout_probe():
@@ -173,23 +205,22 @@ def test_w4a16_tiny_decode():
 
 @pytest.mark.parametrize("li", range(4))
 def test_w4a16_qwen3_decode_all_batches(li):
+    """Every output of every Qwen3-8B-like decode layer at every batch size."""
     q = require_gpu()
     cfg = configs.QWEN3_DECODE
     layer = cfg.layers[li]
     n, k = layer.n, layer.k
-    w = synth.weights(cfg.cid, li, n, k)
+    w, rc, rs = orows.int4_layer(cfg.cid, li, n, k)
     say("w4a16", layer.name, n, k)
     blob = _int4_blob(q, w)
-    cols = sample_rows(n, 512, n + k)
-    rc, rs = int4.quantize(w[cols])
     for m in cfg.ms:
         xb = synth.decode_x_bf16(cfg.cid, li, m, k)
         y16 = q.gemm_w4a16(dev_bf16(xb), blob, n, k, out_dtype=torch.bfloat16)
         y32 = q.gemm_w4a16(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
         torch.cuda.synchronize()
         ref = gemm.w4a16(xb, rc, rs)
-        _check(host_f64(y32)[:, cols], ref, False)
-        _check(host_f64(y16)[:, cols], ref, True)
+        _check(host_f64(y32), ref, False)
+        _check(host_f64(y16), ref, True)
 
 
 @pytest.mark.parametrize("m", [2, 17, 33, 50, 100])
@@ -244,23 +275,22 @@ def test_w4a16_one_hot_layout_probe():
 
 @pytest.mark.parametrize("li", range(3))
 def test_lut2_gemma3_decode(li):
+    """Every output of every Gemma3-12B-like LUT2 layer at every batch size."""
     q = require_gpu()
     cfg = configs.GEMMA3_LUT2
     layer = cfg.layers[li]
     n, k = layer.n, layer.k
-    w = synth.weights(cfg.cid, li, n, k)
+    w, ri, rc = orows.lut2_layer(cfg.cid, li, n, k)
     say("lut2", layer.name, n, k)
     blob = _lut2_blob(q, w)
-    cols = sample_rows(n, 96, n + k)
-    ri, rc = lut2.fit(w[cols])
     for m in cfg.ms:
         xb = synth.decode_x_bf16(cfg.cid, li, m, k)
         y16 = q.gemm_lut2(dev_bf16(xb), blob, n, k, out_dtype=torch.bfloat16)
         y32 = q.gemm_lut2(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
         torch.cuda.synchronize()
         ref = gemm.lut2_gemm(xb, ri, rc)
-        _check(host_f64(y32)[:, cols], ref, False)
-        _check(host_f64(y16)[:, cols], ref, True)
+        _check(host_f64(y32), ref, False)
+        _check(host_f64(y16), ref, True)
 
 
 def test_lut2_one_hot_layout_probe_and_ragged():

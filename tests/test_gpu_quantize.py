@@ -2,19 +2,20 @@
 
 quantize_nvfp4 (activations and weights), quantize_int4_g128 and fit_lut2,
 called through the C ABI on seeded synthetic inputs with the workloads'
-shapes, value distributions and outliers.  At the largest sizes the oracle
-recomputes the tensor scale from the whole tensor and checks a seeded sample
-of rows (always including the last).
+shapes, value distributions and outliers.  Every code and every scale is
+compared, at every size: at the largest ones the oracle runs over row
+chunks in parallel threads (tests/oracle_rows.py), with the tensor scale
+taken over the whole tensor.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from decode_nvfp4_rtn_amd import synth
+from decode_nvfp4_rtn_amd import synth, configs
 from oracle import nvfp4, int4, lut2
-from tests.gpu_common import (require_gpu, say, dev_f32, dev_bf16, host_u8, host_u16,
-                              sample_rows)
+from tests import oracle_rows as orows
+from tests.gpu_common import (require_gpu, say, dev_f32, dev_bf16, host_u8, host_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,18 +48,33 @@ def test_quantize_tiny_fp32_weights():
     _check_nvfp4(q, w, dev_f32(w))
 
 
-@pytest.mark.parametrize("m,k,outl,cfg", [
-    (8192, 4096, "channels", 2),
-    (8192, 12288, "channels", 2),
-    (4096, 17408, "elements", 4),
-    (32768, 5120, "elements", 4),
-])
-def test_quantize_bf16_full_size_sampled(m, k, outl, cfg):
+# The activations the prefill measurements quantize: the Qwen3-8B-like qkv
+# (K = 4096) and down (K = 12288) inputs at M = 8192, and the 27B-class qkv
+# (K = 5120) and down (K = 17408) inputs up to M = 32768 (1.14 GB of bf16).
+@pytest.mark.parametrize("cfg,li,m", [
+    (configs.QWEN3_PREFILL, 0, 8192),
+    (configs.QWEN3_PREFILL, 3, 8192),
+    (configs.BIG27_PREFILL, 3, 4096),
+    (configs.BIG27_PREFILL, 0, 32768),
+    (configs.BIG27_PREFILL, 3, 32768),
+], ids=["qwen3-qkv-8192", "qwen3-down-8192", "27b-down-4096", "27b-qkv-32768",
+        "27b-down-32768"])
+def test_quantize_bf16_full_size_every_row(cfg, li, m):
     q = require_gpu()
-    bits = synth.activations_bf16(cfg, 0, m, k, outliers=outl)
-    xf = synth.bf16_bits_as_f32(bits)
-    say("quantize bf16", m, k, outl)
-    _check_nvfp4(q, xf, dev_bf16(bits), rows=sample_rows(m, 96, m + k))
+    k = cfg.layers[li].k
+    say("quantize bf16 every row", cfg.name, cfg.layers[li].name, m, k)
+    bits = orows.activations_bf16(cfg.cid, li, m, k, outliers=cfg.outliers)
+    codes, scales, st = q.quantize_nvfp4(dev_bf16(bits))
+    torch.cuda.synchronize()
+    gc, gs, gt = host_u8(codes), host_u8(scales), np.float32(st.item())
+    del codes, scales
+    xf = orows.bf16_as_f32(bits)
+    del bits
+    ref_st = nvfp4.tensor_scale(xf)
+    assert gt == ref_st
+    rc, rs, _ = orows.nvfp4_quantize(xf, ref_st)
+    assert orows.first_mismatch(gs, rs) is None, f"scales differ at {orows.first_mismatch(gs, rs)}"
+    assert orows.first_mismatch(gc, rc) is None, f"codes differ at {orows.first_mismatch(gc, rc)}"
 
 
 @pytest.mark.parametrize("m,k", [(1, 16), (3, 48), (17, 1040), (300, 512), (1000, 64)])
@@ -106,17 +122,30 @@ def test_quantize_is_deterministic():
 
 # ------------------------------------------------------------------ INT4 --
 
-@pytest.mark.parametrize("n,k,cfg", [(256, 512, 1), (6144, 4096, 3), (4096, 12288, 3)])
-def test_int4_quantizer_bitexact(n, k, cfg):
+@pytest.mark.parametrize("li", range(4))
+def test_int4_quantizer_bitexact_every_row(li):
+    """The four Qwen3-8B-like decode layers, every row."""
     q = require_gpu()
-    w = synth.weights(cfg, 0, n, k)
-    say("int4 quantize", n, k)
+    cfg = configs.QWEN3_DECODE
+    n, k = cfg.layers[li].n, cfg.layers[li].k
+    w, rc, rs = orows.int4_layer(cfg.cid, li, n, k)
+    say("int4 quantize every row", cfg.layers[li].name, n, k)
     codes, scales = q.quantize_int4_g128(dev_f32(w))
     torch.cuda.synchronize()
-    rows = sample_rows(n, 512, n + k)
-    rc, rs = int4.quantize(w[rows])
-    assert np.array_equal(host_u16(scales)[rows], rs)
-    assert np.array_equal(host_u8(codes)[rows], rc)
+    gs, gc = host_u16(scales), host_u8(codes)
+    assert orows.first_mismatch(gs, rs) is None, f"scales differ at {orows.first_mismatch(gs, rs)}"
+    assert orows.first_mismatch(gc, rc) is None, f"codes differ at {orows.first_mismatch(gc, rc)}"
+
+
+def test_int4_quantizer_tiny():
+    q = require_gpu()
+    w = synth.weights(1, 0, 256, 512)
+    say("int4 quantize tiny")
+    codes, scales = q.quantize_int4_g128(dev_f32(w))
+    torch.cuda.synchronize()
+    rc, rs = int4.quantize(w)
+    assert np.array_equal(host_u16(scales), rs)
+    assert np.array_equal(host_u8(codes), rc)
 
 
 def test_int4_quantizer_edge_groups():
@@ -135,17 +164,33 @@ def test_int4_quantizer_edge_groups():
 
 # ------------------------------------------------------------------ LUT2 --
 
-@pytest.mark.parametrize("n,k", [(64, 3840), (48, 15360), (3840, 3840)])
-def test_lut2_fit_bitexact(n, k):
+@pytest.mark.parametrize("li", range(3))
+def test_lut2_fit_bitexact_every_row(li):
+    """The three Gemma3-12B-like layers (3840 x 3840, 30720 x 3840,
+    3840 x 15360), every row."""
     q = require_gpu()
-    w = synth.weights(5, 0, n, k)
-    say("lut2 fit", n, k)
+    cfg = configs.GEMMA3_LUT2
+    n, k = cfg.layers[li].n, cfg.layers[li].k
+    w, ri, rc = orows.lut2_layer(cfg.cid, li, n, k)
+    say("lut2 fit every row", cfg.layers[li].name, n, k)
     idx, cent = q.fit_lut2(dev_f32(w))
     torch.cuda.synchronize()
-    rows = sample_rows(n, 64, n + k)
-    ri, rc = lut2.fit(w[rows])
-    assert np.array_equal(host_u16(cent)[rows], rc)
-    assert np.array_equal(host_u8(idx)[rows], ri)
+    gcent, gidx = host_u16(cent), host_u8(idx)
+    assert orows.first_mismatch(gcent, rc) is None, f"centroids differ at {orows.first_mismatch(gcent, rc)}"
+    assert orows.first_mismatch(gidx, ri) is None, f"indices differ at {orows.first_mismatch(gidx, ri)}"
+
+
+def test_lut2_fit_long_rows():
+    """Rows of 15360 and 3840 weights drawn from other seeds than the layers."""
+    q = require_gpu()
+    for n, k in [(64, 3840), (48, 15360)]:
+        w = synth.weights(5, 0, n, k)
+        say("lut2 fit", n, k)
+        idx, cent = q.fit_lut2(dev_f32(w))
+        torch.cuda.synchronize()
+        ri, rc = lut2.fit(w)
+        assert np.array_equal(host_u16(cent), rc)
+        assert np.array_equal(host_u8(idx), ri)
 
 
 def test_lut2_fit_special_rows():

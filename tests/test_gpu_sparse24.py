@@ -1,6 +1,6 @@
 """GPU parity of the 2:4 sparse INT4 path against oracle.sparse24.
 
-* quantize_int4_g128_sp24: codes and scales bit-exact (sampled rows at full size).
+* quantize_int4_g128_sp24: codes and scales bit-exact (every row).
 * repack (QL_INT4_SP24) + gemm_w4a16_sp24: fp32 outputs within 1e-3 of the
   output RMS of the oracle's fp64 product, bf16 outputs by the bf16 rule; every
   Qwen3-8B-like decode shape and batch, ragged shapes through both kernels
@@ -14,6 +14,7 @@ import torch
 
 from decode_nvfp4_rtn_amd import synth, configs
 from oracle import int4, sparse24, gemm
+from tests import oracle_rows as orows
 from tests.gpu_common import (require_gpu, say, dev_f32, dev_bf16, host_f64, host_u8, host_u16,
                               sample_rows)
 
@@ -44,10 +45,10 @@ def test_sp24_quantizer_bitexact(n, k, cfg):
     say("sp24 quantize", n, k)
     codes, scales = q.quantize_int4_g128(dev_f32(w), sparse24=True)
     torch.cuda.synchronize()
-    rows = sample_rows(n, 512, n + k)
-    rc, rs = sparse24.quantize(w[rows])
-    assert np.array_equal(host_u16(scales)[rows], rs)
-    assert np.array_equal(host_u8(codes)[rows], rc)
+    rc, rs = orows.sp24_quantize(w)
+    gs, gc = host_u16(scales), host_u8(codes)
+    assert orows.first_mismatch(gs, rs) is None, f"scales differ at {orows.first_mismatch(gs, rs)}"
+    assert orows.first_mismatch(gc, rc) is None, f"codes differ at {orows.first_mismatch(gc, rc)}"
 
 
 def test_sp24_tiny_decode_and_layout_probe():
@@ -80,19 +81,18 @@ def test_sp24_qwen3_decode_all_batches(li):
     cfg = configs.QWEN3_DECODE
     layer = cfg.layers[li]
     n, k = layer.n, layer.k
-    w = synth.weights(cfg.cid, li, n, k)
+    w = orows.int4_layer(cfg.cid, li, n, k)[0]
     say("sp24", layer.name, n, k)
     blob, _, _ = _sp24_blob(q, w)
-    cols = sample_rows(n, 512, n + k)
-    rc, rs = sparse24.quantize(w[cols])
+    rc, rs = orows.sp24_quantize(w)
     for m in cfg.ms:
         xb = synth.decode_x_bf16(cfg.cid, li, m, k)
         y16 = q.gemm_w4a16_sp24(dev_bf16(xb), blob, n, k, out_dtype=torch.bfloat16)
         y32 = q.gemm_w4a16_sp24(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
         torch.cuda.synchronize()
         ref = gemm.w4a16_sp24(xb, rc, rs)
-        _check(host_f64(y32)[:, cols], ref, False)
-        _check(host_f64(y16)[:, cols], ref, True)
+        _check(host_f64(y32), ref, False)
+        _check(host_f64(y16), ref, True)
 
 
 @pytest.mark.parametrize("n,k", [(16 * 1031, 3840), (16 * 1537, 2048), (272, 8320), (6160, 1152)])
