@@ -2,22 +2,29 @@
 """Benchmark of the quantized linear layer on one MI355X; prints ONE JSON line.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-  prefill  the four Qwen3-8B-like layers at M = 8192 tokens, each
+  prefill  the four 27B-class layers (qkv 7168x5120, o_proj 5120x5120,
+           gate_up 34816x5120, down 5120x17408) at M = 32768 tokens, each
            quantize_nvfp4(X bf16) -> gemm_w4a4(-> Y bf16)     (quantize is timed)
-  decode   the same four layer shapes, W4A16 (INT4 group-128) at M = 16
-  decode   the three Gemma3-12B-like layers, LUT2 at M = 8
-Inputs and packed weights are resident in HBM before the timed region.
+  decode   W4A16 (INT4 group-128) at M = 16 over the four Qwen3-8B-like shapes
+  decode   LUT2 at M = 8 over the three Gemma3-12B-like shapes
+The activations are drawn at full size by the seeded generator (synth),
+every row, in host threads; inputs and packed weights are resident in HBM
+before the timed region.
 
-value = the step's algorithmic FLOPs / ms_per_step (TFLOP/s); the prefill
-FLOPs dominate (decode adds < 0.3 %).  ``parts`` breaks the step down with HIP
-events (torch.cuda.Event on the stream every kernel is launched on):
-per-layer quantize and GEMM times, the GEMM-only TFLOP/s as fractions of the
-fp16 (the dtype the MFMAs run), FP8 and FP4 dense peaks, and a separate
-decode sweep (all batch sizes) that rotates through > 512 MiB of weight copies
-so the 256 MiB Infinity Cache cannot serve repeats.
+value = the step's algorithmic FLOPs / ms_per_step (TFLOP/s; the prefill
+FLOPs are 99.99 % of them).  HIP events recorded on the stream every kernel is
+launched on time each quantize, each GEMM and the decode block.
 
-``roofline`` describes the dominant kernel (gemm_w4a4); ``cpu_baseline`` times
-the CPU oracle (test infrastructure) on a bounded sample of the same workload.
+``roofline`` describes the dominant kernel, the W4A4 GEMM
+(w4a4_coop_kernel), against the dense FP4 peak the metric names (its fp16
+fraction, the rate of the MFMA it runs on, is reported beside it);
+``cpu_baseline`` times the CPU oracle (test infrastructure) on a bounded
+sample of the same workload.  ``parts`` holds the other measurements: the
+Qwen3-8B-like prefill set at M = 8192, the 27B-class set at M = 4096 and
+16384, smaller prefill batches, a decode sweep over every batch size that
+rotates through > 512 MiB of weight copies (so the 256 MiB Infinity Cache
+cannot serve repeats), the 2:4 sparse decode, torch's bf16 GEMM/GEMV on the
+same shapes, and weight streaming from host memory.
 """
 
 import argparse
@@ -55,10 +62,15 @@ def _kernel_build_hash():
     return h.hexdigest()[:16]
 
 
-def _traffic_record():
-    """HBM traffic of the dominant kernel from the committed rocprofv3 --pmc
-    summary, if it was taken on the kernel as built now (hash match)."""
-    path = os.path.join(ROOT, "profiles", "gemm_w4a4_qwen3_traffic.md")
+TRAFFIC_PROFILE = {"27b": os.path.join("profiles", "gemm_w4a4_27b_m32768_traffic.md"),
+                   "qwen3": os.path.join("profiles", "gemm_w4a4_qwen3_m8192_traffic.md")}
+
+
+def _traffic_record(prefill_set):
+    """HBM bytes per launch of the dominant kernel on the step's prefill set,
+    from the committed rocprofv3 --pmc summary, if it was taken on the kernel
+    as built now (hash match)."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE[prefill_set])
     if not os.path.exists(path):
         return None
     rec = {}
@@ -72,6 +84,45 @@ def _traffic_record():
     return float(rec["bytes_per_launch"])
 
 
+def host_threads():
+    """Cores this process may run on (the GPU machine's share of the host)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def draw_activations_bf16(cid, li, m, k, outliers):
+    """synth.activations_bf16 of every row of [m, k], drawn in 2048-row
+    ranges on host threads (synth seeds each 256-row block on its own, so this
+    is the same tensor as one draw)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from decode_nvfp4_rtn_amd import synth
+    out = np.empty((m, k), dtype=np.uint16)
+    step = 2048
+
+    def one(r0):
+        out[r0:min(m, r0 + step)] = synth.activations_bf16(cid, li, m, k, outliers=outliers,
+                                                           rows=(r0, min(m, r0 + step)))
+    with ThreadPoolExecutor(max_workers=max(1, min(16, host_threads()))) as ex:
+        list(ex.map(one, range(0, m, step)))
+    return out
+
+
+def draw_weights(cid, li, n, k):
+    """synth.weights of every row of [n, k], drawn in row ranges on host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    from decode_nvfp4_rtn_amd import synth
+    out = np.empty((n, k), dtype=np.float32)
+    step = 2048
+
+    def one(r0):
+        out[r0:min(n, r0 + step)] = synth.weights(cid, li, n, k, rows=(r0, min(n, r0 + step)))
+    with ThreadPoolExecutor(max_workers=max(1, min(16, host_threads()))) as ex:
+        list(ex.map(one, range(0, n, step)))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,12 +130,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-reps", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="rows of X per layer in the CPU-oracle sample")
+                    help="token rows per layer in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-sweep", action="store_true")
     ap.add_argument("--no-bf16-reference", action="store_true")
-    ap.add_argument("--no-27b", action="store_true",
-                    help="skip the 27B-class prefill measurement (M = 4096, 16384, 32768)")
+    ap.add_argument("--prefill-set", choices=("27b", "qwen3"), default="27b",
+                    help="prefill layers of the timed step: the 27B-class set at M = 32768 "
+                         "(default) or the Qwen3-8B-like set at M = 8192 (for profiling that "
+                         "set alone; the other prefill measurements are then skipped)")
+    ap.add_argument("--no-qwen3", action="store_true",
+                    help="skip the Qwen3-8B-like prefill set (M = 8192) and the smaller batches")
+    ap.add_argument("--no-27b-smaller", action="store_true",
+                    help="skip the 27B-class prefill set at M = 4096 and 16384")
     ap.add_argument("--no-small-m", action="store_true",
                     help="skip the smaller prefill batches (M = 512 / 1024 / 2048)")
     ap.add_argument("--no-odp", action="store_true",
@@ -124,41 +181,105 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    def prefill_set(cfg, m_max, ms):
+        """Packed weights, full-size activations and output buffers of a
+        prefill layer set, with a k-split workspace for every M that has one."""
+        out = []
+        for li, L in enumerate(cfg.layers):
+            x = bf16(draw_activations_bf16(cfg.cid, li, m_max, L.k, cfg.outliers))
+            wc, ws, wt = qlin.quantize_nvfp4(f32(draw_weights(cfg.cid, li, L.n, L.k)))
+            blob = qlin.repack_weights(qlin.QL_NVFP4, L.n, L.k, wc, ws, wt)
+            del wc, ws
+            gws_bytes = {m: qlin.gemm_w4a4_workspace(m, L.n, L.k) for m in ms}
+            nb = max(gws_bytes.values())
+            out.append(dict(L=L, x=x, blob=blob, gws_bytes=gws_bytes,
+                            gws=torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None,
+                            codes=torch.empty((m_max, L.k // 2), dtype=torch.uint8, device=dev),
+                            scales=torch.empty((m_max, L.k // 16), dtype=torch.uint8, device=dev),
+                            ts=torch.empty(1, dtype=torch.float32, device=dev),
+                            ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(m_max, L.k)),
+                                           dtype=torch.uint8, device=dev),
+                            y=torch.empty((m_max, L.n), dtype=torch.bfloat16, device=dev)))
+        return out
+
+    def prefill_layer(r, m, ev=None):
+        """quantize_nvfp4 + gemm_w4a4 of one layer on its first m token rows;
+        ev = (e0, e1, e2) events around the two calls."""
+        L = r["L"]
+        if ev is not None:
+            ev[0].record()
+        qlin.quantize_nvfp4(r["x"][:m], codes=r["codes"][:m], scales=r["scales"][:m],
+                            workspace=r["ws"], ts_out=r["ts"])
+        if ev is not None:
+            ev[1].record()
+        qlin.gemm_w4a4(r["codes"][:m], r["scales"][:m], r["ts"], r["blob"], m, L.n, L.k,
+                       y=r["y"][:m], workspace=r["gws"] if r["gws_bytes"][m] else None)
+        if ev is not None:
+            ev[2].record()
+
+    E = torch.cuda.Event
+
+    def interleaved(R, ms, rounds=6, warm=2):
+        """quantize + GEMM of every (M, layer), round-robin in this process:
+        `warm` warm-up rounds, then the median of `rounds` rounds per case."""
+        tq = {(m, i): [] for m in ms for i in range(len(R))}
+        tg = {(m, i): [] for m in ms for i in range(len(R))}
+        for rep in range(rounds + warm):
+            for m in ms:
+                for i, r in enumerate(R):
+                    ev = (E(enable_timing=True), E(enable_timing=True), E(enable_timing=True))
+                    prefill_layer(r, m, ev)
+                    if rep >= warm:
+                        tq[(m, i)].append((ev[0], ev[1]))
+                        tg[(m, i)].append((ev[1], ev[2]))
+        torch.cuda.synchronize()
+        res = {}
+        for m in ms:
+            rows, fl_all, q_all, g_all = [], 0.0, 0.0, 0.0
+            for i, r in enumerate(R):
+                L = r["L"]
+                q = float(np.median([a.elapsed_time(b) for a, b in tq[(m, i)]]))
+                g = float(np.median([a.elapsed_time(b) for a, b in tg[(m, i)]]))
+                fl = 2.0 * m * L.n * L.k
+                fl_all, q_all, g_all = fl_all + fl, q_all + q, g_all + g
+                qbytes = 2.0 * m * L.k + m * L.k / 2 + m * L.k / 16
+                rows.append({"layer": L.name, "n": L.n, "k": L.k, "gemm_us": round(g * 1e3, 1),
+                             "gemm_tflops": round(fl / g / 1e9, 1),
+                             "quantize_us": round(q * 1e3, 1),
+                             "quantize_gbps_1pass_bytes": round(qbytes / q / 1e6, 1),
+                             "k_split_workspace_mb": round(r["gws_bytes"][m] / 1e6, 1)})
+            res[f"m{m}"] = {
+                "layers": rows,
+                "gemm_tflops": round(fl_all / g_all / 1e9, 1),
+                "prefill_tflops_incl_quantize": round(fl_all / (g_all + q_all) / 1e9, 1),
+                "gemm_frac_fp4_peak": round(fl_all / g_all / 1e9 / PEAK["fp4"], 4),
+                "gemm_frac_fp8_peak": round(fl_all / g_all / 1e9 / PEAK["fp8"], 4),
+                "gemm_frac_f16_peak": round(fl_all / g_all / 1e9 / PEAK["f16"], 4),
+                "quantize_ms": round(q_all, 4), "gemm_ms": round(g_all, 4)}
+        return res
+
     # ------------------------------------------------------------ set-up --
-    pre = configs.QWEN3_PREFILL
+    big = configs.BIG27_PREFILL if args.prefill_set == "27b" else configs.QWEN3_PREFILL
     dec = configs.QWEN3_DECODE
     lut = configs.GEMMA3_LUT2
-    M = pre.ms[0]
+    M = max(big.ms)          # 32768 tokens (8192 for the Qwen3-8B-like set)
     M_DEC, M_LUT = 16, 8
 
-    P = []   # prefill layers
-    for li, L in enumerate(pre.layers):
-        x = bf16(synth.activations_bf16(pre.cid, li, M, L.k, outliers=pre.outliers))
-        wc, ws, wt = qlin.quantize_nvfp4(f32(synth.weights(pre.cid, li, L.n, L.k)))
-        blob = qlin.repack_weights(qlin.QL_NVFP4, L.n, L.k, wc, ws, wt)
-        del wc, ws
-        P.append(dict(L=L, x=x, blob=blob,
-                      codes=torch.empty((M, L.k // 2), dtype=torch.uint8, device=dev),
-                      scales=torch.empty((M, L.k // 16), dtype=torch.uint8, device=dev),
-                      ts=torch.empty(1, dtype=torch.float32, device=dev),
-                      ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(M, L.k)),
-                                     dtype=torch.uint8, device=dev),
-                      y=torch.empty((M, L.n), dtype=torch.bfloat16, device=dev)))
-        gb = qlin.gemm_w4a4_workspace(M, L.n, L.k)   # 0 when the tiles fill whole rounds
-        P[-1]["gws"] = torch.empty(gb, dtype=torch.uint8, device=dev) if gb else None
+    R = prefill_set(big, M, big.ms)
     D = []   # W4A16 decode layers
     for li, L in enumerate(dec.layers):
-        c, s = qlin.quantize_int4_g128(f32(synth.weights(dec.cid, li, L.n, L.k)))
+        w = f32(draw_weights(dec.cid, li, L.n, L.k))
+        c, s = qlin.quantize_int4_g128(w)
         blob = qlin.repack_weights(qlin.QL_INT4_G128, L.n, L.k, c, s)
-        x32 = {m: bf16(synth.decode_x_bf16(dec.cid, li, m, L.k)) for m in dec.ms}
-        c24, s24 = qlin.quantize_int4_g128(f32(synth.weights(dec.cid, li, L.n, L.k)), sparse24=True)
+        c24, s24 = qlin.quantize_int4_g128(w, sparse24=True)
         blob24 = qlin.repack_weights(qlin.QL_INT4_SP24, L.n, L.k, c24, s24)
-        del c24, s24
+        del w, c, s, c24, s24
+        x32 = {m: bf16(synth.decode_x_bf16(dec.cid, li, m, L.k)) for m in dec.ms}
         D.append(dict(L=L, blob=blob, blob24=blob24, x=x32,
                       y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in dec.ms}))
     U = []   # LUT2 decode layers
     for li, L in enumerate(lut.layers):
-        i, c = qlin.fit_lut2(f32(synth.weights(lut.cid, li, L.n, L.k)))
+        i, c = qlin.fit_lut2(f32(draw_weights(lut.cid, li, L.n, L.k)))
         blob = qlin.repack_weights(qlin.QL_LUT2, L.n, L.k, i, c)
         xs = {m: bf16(synth.decode_x_bf16(lut.cid, li, m, L.k)) for m in lut.ms}
         U.append(dict(L=L, blob=blob, x=xs,
@@ -166,41 +287,30 @@ def main():
     torch.cuda.synchronize()
 
     _progress("inputs and packed weights resident")
-    prefill_flops = sum(2.0 * M * p["L"].n * p["L"].k for p in P)
+    prefill_flops = sum(2.0 * M * r["L"].n * r["L"].k for r in R)
     dec_flops = sum(2.0 * M_DEC * d["L"].n * d["L"].k for d in D)
     lut_flops = sum(2.0 * M_LUT * u["L"].n * u["L"].k for u in U)
     step_flops = prefill_flops + dec_flops + lut_flops
 
-    E = torch.cuda.Event
-
     def step(ev=None):
-        for i, p in enumerate(P):
-            L = p["L"]
-            if ev is not None:
-                ev[i][0].record()
-            qlin.quantize_nvfp4(p["x"], codes=p["codes"], scales=p["scales"],
-                                workspace=p["ws"], ts_out=p["ts"])
-            if ev is not None:
-                ev[i][1].record()
-            qlin.gemm_w4a4(p["codes"], p["scales"], p["ts"], p["blob"], M, L.n, L.k, y=p["y"],
-                           workspace=p["gws"])
-            if ev is not None:
-                ev[i][2].record()
+        for i, r in enumerate(R):
+            prefill_layer(r, M, None if ev is None else ev[i])
         if ev is not None:
-            ev[len(P)][0].record()
+            ev[len(R)][0].record()
         for d in D:
             qlin.gemm_w4a16(d["x"][M_DEC], d["blob"], d["L"].n, d["L"].k, y=d["y"][M_DEC])
         for u in U:
             qlin.gemm_lut2(u["x"][M_LUT], u["blob"], u["L"].n, u["L"].k, y=u["y"][M_LUT])
         if ev is not None:
-            ev[len(P)][1].record()
+            ev[len(R)][1].record()
 
     # -------------------------------------------------- warm-up + timing --
-    # The timed region is K eager steps.  HIP events recorded on the stream the
-    # kernels run on bracket every quantize, every GEMM and the decode block;
-    # the host stays ahead of the GPU (each step queues ~3 ms of work for
-    # ~0.2 ms of launch calls), so the events see back-to-back kernels.
-    evs = [[[E(enable_timing=True) for _ in range(3)] for _ in range(len(P) + 1)]
+    # The timed region is K eager steps between two device synchronisations.
+    # HIP events recorded on the stream the kernels run on bracket every
+    # quantize, every GEMM and the decode block; the host stays ahead of the
+    # GPU (each step queues ~17 ms of work for well under 1 ms of launch
+    # calls), so the events see back-to-back kernels.
+    evs = [[[E(enable_timing=True) for _ in range(3)] for _ in range(len(R) + 1)]
            for _ in range(args.steps)]
     for _ in range(args.warmup):
         step()
@@ -211,24 +321,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    q_ms = np.array([[evs[s][i][0].elapsed_time(evs[s][i][1]) for i in range(len(P))]
+    q_ms = np.array([[evs[s][i][0].elapsed_time(evs[s][i][1]) for i in range(len(R))]
                      for s in range(args.steps)])
-    g_ms = np.array([[evs[s][i][1].elapsed_time(evs[s][i][2]) for i in range(len(P))]
+    g_ms = np.array([[evs[s][i][1].elapsed_time(evs[s][i][2]) for i in range(len(R))]
                      for s in range(args.steps)])
-    d_ms = np.array([evs[s][len(P)][0].elapsed_time(evs[s][len(P)][1]) for s in range(args.steps)])
+    d_ms = np.array([evs[s][len(R)][0].elapsed_time(evs[s][len(R)][1]) for s in range(args.steps)])
     _progress(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
     layers = []
-    for i, p in enumerate(P):
-        L = p["L"]
+    for i, r in enumerate(R):
+        L = r["L"]
         fl = 2.0 * M * L.n * L.k
         gq = float(np.median(g_ms[:, i]))
         qq = float(np.median(q_ms[:, i]))
         qbytes = 2.0 * M * L.k + M * L.k / 2 + M * L.k / 16
         layers.append({
             "layer": L.name, "n": L.n, "k": L.k,
-            "gemm_us": round(gq * 1e3, 2), "gemm_tflops": round(fl / gq / 1e9, 1),
-            "quantize_us": round(qq * 1e3, 2),
+            "gemm_us": round(gq * 1e3, 1), "gemm_tflops": round(fl / gq / 1e9, 1),
+            "gemm_frac_fp4_peak": round(fl / gq / 1e9 / PEAK["fp4"], 4),
+            "gemm_frac_f16_peak": round(fl / gq / 1e9 / PEAK["f16"], 4),
+            "quantize_us": round(qq * 1e3, 1),
             "quantize_gbps_1pass_bytes": round(qbytes / qq / 1e6, 1),
             "prefill_tflops_incl_quantize": round(fl / (gq + qq) / 1e9, 1),
         })
@@ -236,6 +348,42 @@ def main():
     quant_ms_step = float(np.median(q_ms.sum(axis=1)))
     gemm_tflops = prefill_flops / gemm_ms_step / 1e9
     prefill_tflops = prefill_flops / (gemm_ms_step + quant_ms_step) / 1e9
+    # mean event-timed duration of the 4 x K timed GEMM launches
+    avg_launch_ms = float(np.mean(g_ms))
+    achieved = (prefill_flops / len(R)) / avg_launch_ms / 1e9
+
+    # ---------------------------------- 27B-class set at smaller M ------
+    big_parts = {f"m{M}": {"layers": layers, "gemm_tflops": round(gemm_tflops, 1),
+                            "prefill_tflops_incl_quantize": round(prefill_tflops, 1),
+                            "gemm_frac_fp4_peak": round(gemm_tflops / PEAK["fp4"], 4),
+                            "gemm_frac_fp8_peak": round(gemm_tflops / PEAK["fp8"], 4),
+                            "gemm_frac_f16_peak": round(gemm_tflops / PEAK["f16"], 4),
+                            "quantize_ms": round(quant_ms_step, 4),
+                            "gemm_ms": round(gemm_ms_step, 4),
+                            "source": "the timed steps (median per layer)"}}
+    if not args.no_27b_smaller and args.prefill_set == "27b":
+        big_parts.update(interleaved(R, [m for m in big.ms if m != M]))
+        for m in big.ms:
+            if m != M:
+                _progress(f"27b m={m}: GEMM {big_parts[f'm{m}']['gemm_tflops']} TFLOP/s")
+    big_parts["activations"] = (f"every row drawn by the seeded generator at M = {M}; smaller "
+                                "M are its first rows (the same tensors as draws at those M)")
+
+    # ----------------------------------- Qwen3-8B-like prefill set ------
+    qwen = {}
+    P = []
+    if args.prefill_set == "qwen3":
+        qwen, big_parts, P = big_parts, {}, R
+    elif not args.no_qwen3:
+        pre = configs.QWEN3_PREFILL
+        SM = () if args.no_small_m else (512, 1024, 2048)
+        P = prefill_set(pre, pre.ms[0], (pre.ms[0],) + SM)
+        qwen = interleaved(P, [pre.ms[0]])
+        _progress(f"qwen3 m={pre.ms[0]}: GEMM {qwen[f'm{pre.ms[0]}']['gemm_tflops']} TFLOP/s")
+        if SM:
+            qwen.update(interleaved(P, list(SM)))
+        qwen["activations"] = ("every row drawn by the seeded generator at M = 8192; smaller M "
+                               "are its first rows")
 
     # --------------------------------------- decode sweep (MALL defeated) --
     # Each (layer, batch) case is captured once in a HIP graph that launches the
@@ -309,7 +457,7 @@ def main():
     # the stack with resident weights, of the block copies alone, and of the
     # streamed stack; `exposed` is what the copies add.
     odp = {}
-    if not args.no_odp:
+    if not args.no_odp and P:
         from decode_nvfp4_rtn_amd.pipeline import PrefillWeightStream
         ODP_BLOCKS = 4
         host = [p["blob"].cpu().pin_memory() for p in P]
@@ -380,160 +528,37 @@ def main():
         odp["block_weights_mb"] = round(wbytes / 1e6, 1)
         del streamer, host
 
-    # ------------------------------- 27B-class long-context prefill ----
-    # NVFP4 W4A4 prefill (quantize + GEMM, bf16 out) of the 27B-class layer
-    # set at M = 4096, 16384 and 32768 tokens, interleaved round-robin over
-    # sizes and layers in this one process.  Activations: the first 4096 rows
-    # of each layer's seeded draw (N(0,1), 0.1 % of elements x50, bf16),
-    # repeated down to M rows (timing does not depend on the values; drawing
-    # 1.1 G values on the host would take longer than the whole measurement).
-    big = {}
-    if not args.no_27b:
-        b27 = configs.BIG27_PREFILL
-        MB = max(b27.ms)
-        R = []
-        for li, L in enumerate(b27.layers):
-            x0 = bf16(synth.activations_bf16(b27.cid, li, 4096, L.k, outliers=b27.outliers))
-            x = x0.repeat(MB // 4096, 1)
-            del x0
-            wc, ws, wt = qlin.quantize_nvfp4(f32(synth.weights(b27.cid, li, L.n, L.k)))
-            blob = qlin.repack_weights(qlin.QL_NVFP4, L.n, L.k, wc, ws, wt)
-            del wc, ws
-            R.append(dict(L=L, x=x, blob=blob,
-                          codes=torch.empty((MB, L.k // 2), dtype=torch.uint8, device=dev),
-                          scales=torch.empty((MB, L.k // 16), dtype=torch.uint8, device=dev),
-                          ts=torch.empty(1, dtype=torch.float32, device=dev),
-                          ws=torch.empty(max(16, qlin.quantize_nvfp4_workspace(MB, L.k)),
-                                         dtype=torch.uint8, device=dev),
-                          y=torch.empty((MB, L.n), dtype=torch.bfloat16, device=dev)))
-            # k split of a partly filled last round of tiles (fp32 partials)
-            R[-1]["gws_bytes"] = {m: qlin.gemm_w4a4_workspace(m, L.n, L.k) for m in b27.ms}
-            nb = max(R[-1]["gws_bytes"].values())
-            R[-1]["gws"] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-        torch.cuda.synchronize()
-        _progress("27B-class inputs and packed weights resident")
-        reps = 5
-        tq = {(m, i): [] for m in b27.ms for i in range(len(R))}
-        tg = {(m, i): [] for m in b27.ms for i in range(len(R))}
-        for rep in range(reps + 1):
-            for m in b27.ms:
-                for i, r in enumerate(R):
-                    L = r["L"]
-                    e0, e1, e2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
-                    e0.record()
-                    qlin.quantize_nvfp4(r["x"][:m], codes=r["codes"][:m], scales=r["scales"][:m],
-                                        workspace=r["ws"], ts_out=r["ts"])
-                    e1.record()
-                    qlin.gemm_w4a4(r["codes"][:m], r["scales"][:m], r["ts"], r["blob"], m, L.n, L.k,
-                                   y=r["y"][:m],
-                                   workspace=r["gws"] if r["gws_bytes"][m] else None)
-                    e2.record()
-                    if rep > 0:   # the first round is a warm-up
-                        tq[(m, i)].append((e0, e1))
-                        tg[(m, i)].append((e1, e2))
-        torch.cuda.synchronize()
-        for m in b27.ms:
-            rows, fl_all, q_all, g_all = [], 0.0, 0.0, 0.0
-            for i, r in enumerate(R):
-                L = r["L"]
-                q = float(np.median([a.elapsed_time(b) for a, b in tq[(m, i)]]))
-                g = float(np.median([a.elapsed_time(b) for a, b in tg[(m, i)]]))
-                fl = 2.0 * m * L.n * L.k
-                fl_all, q_all, g_all = fl_all + fl, q_all + q, g_all + g
-                rows.append({"layer": L.name, "n": L.n, "k": L.k, "gemm_us": round(g * 1e3, 1),
-                             "gemm_tflops": round(fl / g / 1e9, 1), "quantize_us": round(q * 1e3, 1),
-                             "k_split_workspace_mb": round(r["gws_bytes"][m] / 1e6, 1)})
-            big[f"m{m}"] = {
-                "layers": rows,
-                "gemm_tflops": round(fl_all / g_all / 1e9, 1),
-                "prefill_tflops_incl_quantize": round(fl_all / (g_all + q_all) / 1e9, 1),
-                "gemm_frac_f16_peak": round(fl_all / g_all / 1e9 / PEAK["f16"], 4),
-                "gemm_frac_fp8_peak": round(fl_all / g_all / 1e9 / PEAK["fp8"], 4),
-                "gemm_frac_fp4_peak": round(fl_all / g_all / 1e9 / PEAK["fp4"], 4),
-                "quantize_ms": round(q_all, 4), "gemm_ms": round(g_all, 4)}
-            _progress(f"27b m={m}: GEMM {big[f'm{m}']['gemm_tflops']} TFLOP/s, "
-                      f"with quantize {big[f'm{m}']['prefill_tflops_incl_quantize']}")
-        big["activations"] = ("first 4096 rows of each layer's seeded draw repeated to M rows; "
-                              "median of 5 interleaved rounds after one warm-up round")
-        del R
-        torch.cuda.empty_cache()
-
-    # ------------------------------------------ smaller prefill batches ----
-    # The Qwen3-8B-like layers at M = 512 / 1024 / 2048 (the first M rows of
-    # the same inputs), quantize + GEMM, with a gemm_w4a4 workspace where a k
-    # split applies.  With fewer 256 x 256 tiles than CUs these show the
-    # GEMM's dispatch: the cooperative kernel above half a round of tiles,
-    # its k split below that (workspace), never the per-wave kernel here.
-    small = {}
-    if not args.no_small_m:
-        SM = (512, 1024, 2048)
-        gws = {}
-        for i, p in enumerate(P):
-            for m in SM:
-                nb = qlin.gemm_w4a4_workspace(m, p["L"].n, p["L"].k)
-                gws[(m, i)] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
-        tq = {(m, i): [] for m in SM for i in range(len(P))}
-        tg = {(m, i): [] for m in SM for i in range(len(P))}
-        for rep in range(6):
-            for m in SM:
-                for i, p in enumerate(P):
-                    L = p["L"]
-                    e0, e1, e2 = E(enable_timing=True), E(enable_timing=True), E(enable_timing=True)
-                    e0.record()
-                    qlin.quantize_nvfp4(p["x"][:m], codes=p["codes"][:m], scales=p["scales"][:m],
-                                        workspace=p["ws"], ts_out=p["ts"])
-                    e1.record()
-                    qlin.gemm_w4a4(p["codes"][:m], p["scales"][:m], p["ts"], p["blob"], m, L.n, L.k,
-                                   y=p["y"][:m], workspace=gws[(m, i)])
-                    e2.record()
-                    if rep > 0:   # the first round is a warm-up
-                        tq[(m, i)].append((e0, e1))
-                        tg[(m, i)].append((e1, e2))
-        torch.cuda.synchronize()
-        for m in SM:
-            rows, fl_all, q_all, g_all = [], 0.0, 0.0, 0.0
-            for i, p in enumerate(P):
-                L = p["L"]
-                q = float(np.median([a.elapsed_time(b) for a, b in tq[(m, i)]]))
-                g = float(np.median([a.elapsed_time(b) for a, b in tg[(m, i)]]))
-                fl = 2.0 * m * L.n * L.k
-                fl_all, q_all, g_all = fl_all + fl, q_all + q, g_all + g
-                nb = 0 if gws[(m, i)] is None else gws[(m, i)].numel()
-                rows.append({"layer": L.name, "gemm_us": round(g * 1e3, 1),
-                             "gemm_tflops": round(fl / g / 1e9, 1), "quantize_us": round(q * 1e3, 1),
-                             "k_split_workspace_mb": round(nb / 1e6, 1)})
-            small[f"m{m}"] = {"layers": rows, "gemm_tflops": round(fl_all / g_all / 1e9, 1),
-                              "prefill_tflops_incl_quantize": round(fl_all / (g_all + q_all) / 1e9, 1)}
-            _progress(f"small m={m}: GEMM {small[f'm{m}']['gemm_tflops']} TFLOP/s")
-        small["activations"] = "first M rows of the M = 8192 inputs; median of 5 interleaved rounds"
-        del gws
-
     # ------------------------------------------- BF16 reference points ----
     # The pages state their speed-ups against BF16; torch's bf16 matmul
     # (hipBLASLt) on the same shapes is that reference here: prefill
-    # Y = X W^T at M=8192 (TFLOP/s) and decode GEMV at M=1 and 16 (GB/s,
-    # weights rotated over > 600 MB like the decode sweep).
+    # Y = X W^T on the 27B-class set at M = 32768 and the Qwen3-8B-like set at
+    # M = 8192 (TFLOP/s), and decode GEMV at M = 1 and 16 (GB/s, weights
+    # rotated over > 600 MB like the decode sweep).
     bf16_ref = {}
     if not args.no_bf16_reference:
-        for p in P:
-            L = p["L"]
-            wb = torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev) * (L.k ** -0.5)
-            ref_ms = []
-            for _ in range(3):
-                torch.matmul(p["x"], wb.t())
-            torch.cuda.synchronize()
-            for _ in range(10):
-                a, b = E(enable_timing=True), E(enable_timing=True)
-                a.record()
-                torch.matmul(p["x"], wb.t())
-                b.record()
-                b.synchronize()
-                ref_ms.append(a.elapsed_time(b))
-            med = float(np.median(ref_ms))
-            bf16_ref[f"prefill/{L.name}"] = {
-                "us": round(med * 1e3, 1),
-                "tflops": round(2.0 * M * L.n * L.k / med / 1e9, 1)}
-            del wb
+        sets = (("qwen3", P, 8192),) if args.prefill_set == "qwen3" else \
+            (("27b", R, M), ("qwen3", P, 8192))
+        for tag, S, m in sets:
+            for r in S:
+                L = r["L"]
+                wb = torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev) * (L.k ** -0.5)
+                yb = torch.empty((m, L.n), dtype=torch.bfloat16, device=dev)
+                ref_ms = []
+                for _ in range(3):
+                    torch.matmul(r["x"][:m], wb.t(), out=yb)
+                torch.cuda.synchronize()
+                for _ in range(10):
+                    a, b = E(enable_timing=True), E(enable_timing=True)
+                    a.record()
+                    torch.matmul(r["x"][:m], wb.t(), out=yb)
+                    b.record()
+                    b.synchronize()
+                    ref_ms.append(a.elapsed_time(b))
+                med = float(np.median(ref_ms))
+                bf16_ref[f"prefill_{tag}/{L.name}"] = {
+                    "us": round(med * 1e3, 1),
+                    "tflops": round(2.0 * m * L.n * L.k / med / 1e9, 1)}
+                del wb, yb
         for d in D:
             L = d["L"]
             copies = [torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev)
@@ -567,14 +592,17 @@ def main():
             torch.cuda.empty_cache()
         _progress("bf16 reference points measured")
 
+    def speedup(tag, gemm_us):
+        ref = [v["us"] for k, v in bf16_ref.items() if k.startswith(f"prefill_{tag}/")]
+        return round(sum(ref) / gemm_us, 3) if ref else None
+
     # --------------------------------------------------- CPU baseline ----
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_rows, pre, M)
+        cpu = cpu_baseline(args.cpu_rows, big, M)
         _progress(f"cpu baseline: {cpu['sample']}")
 
-    traffic = _traffic_record()
-    avg_launch_ms = gemm_ms_step / len(P)
+    traffic = _traffic_record(args.prefill_set)
     out = {
         "metric": METRIC,
         "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
@@ -589,24 +617,36 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "Qwen3-8B-like linear set: NVFP4 W4A4 prefill (quantize + GEMM, M=8192, "
-                        "bf16 out) over qkv/o/gate_up/down, + W4A16 decode M=16 over the same "
-                        "shapes, + Gemma3-12B-like LUT2 decode M=8",
+            "workload": (("27B-class long-context prefill" if args.prefill_set == "27b" else
+                          "Qwen3-8B-like prefill") +
+                         f", NVFP4 W4A4 (quantize + GEMM, bf16 out) at M={M} tokens over "
+                         "qkv/o_proj/gate_up/down, + W4A16 decode M=16 over the Qwen3-8B-like "
+                         "shapes, + Gemma3-12B-like LUT2 decode M=8"),
             "m_prefill": M, "m_w4a16": M_DEC, "m_lut2": M_LUT,
-            "prefill_layers_nk": [[p["L"].n, p["L"].k] for p in P],
-            "lut2_layers_nk": [[u["L"].n, u["L"].k] for u in U],
+            "prefill_layers_nk": [[L.n, L.k] for L in big.layers],
+            "w4a16_layers_nk": [[L.n, L.k] for L in dec.layers],
+            "lut2_layers_nk": [[L.n, L.k] for L in lut.layers],
+            "activations": ("N(0,1), " + ("0.1% of elements x50" if args.prefill_set == "27b"
+                                          else "1% of channels x10") +
+                            ", bf16; every row drawn by the seeded generator"),
         },
         "roofline": {
             "kernel": "w4a4_coop_kernel (gemm_w4a4)",
             "bound": "mfma",
-            "achieved": round(gemm_tflops, 1),
-            "peak": PEAK["f16"],
+            "achieved": round(achieved, 1),
+            "peak": PEAK["fp4"],
             "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK["f16"], 4),
+            "frac": round(achieved / PEAK["fp4"], 4),
+            "frac_f16_peak": round(achieved / PEAK["f16"], 4),
             "traffic": traffic,
             "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-            "per_launch": "mean over the 4 prefill layers of 2*M*N*K FLOPs / mean event-timed "
-                          "launch duration; traffic = HBM bytes per launch (mean over the layers)",
+            "per_launch": f"2*M*N*K FLOPs per launch averaged over the 4 layers "
+                          f"({prefill_flops / len(R) / 1e12:.2f} TFLOP) / "
+                          "mean event-timed duration of the timed launches; peak = dense FP4 "
+                          "MFMA (the exact NVFP4 products run on the fp16 MFMA, whose dense "
+                          "peak of 2500 TFLOP/s gives frac_f16_peak); traffic = HBM bytes per "
+                          "launch averaged over the layers, from " +
+                          TRAFFIC_PROFILE[args.prefill_set],
         },
         "cpu_baseline": cpu,
         "parts": {
@@ -618,18 +658,18 @@ def main():
             "quantize_ms_per_step": round(quant_ms_step, 4),
             "gemm_ms_per_step": round(gemm_ms_step, 4),
             "decode_block_ms_per_step": round(float(np.median(d_ms)), 4),
-            "layers": layers,
+            "w4a4_gemm_speedup_vs_bf16": speedup(args.prefill_set, gemm_ms_step * 1e3),
+            "prefill_27b": big_parts,
+            "prefill_qwen3": qwen,
+            "w4a4_gemm_speedup_vs_bf16_qwen3_m8192": (
+                speedup("qwen3", sum(l["gemm_us"] for l in qwen["m8192"]["layers"]))
+                if "m8192" in qwen else None),
             "w4a16_gbps_mean_over_layers": _agg("w4a16", dec.ms),
             "lut2_gbps_mean_over_layers": _agg("lut2", lut.ms),
             "w4a16_sp24_gbps_mean_over_layers": _agg("w4a16_sp24", dec.ms),
             "decode_sweep": sweep,
             "bf16_reference": bf16_ref,
             "odp_weight_streaming": odp,
-            "prefill_27b": big,
-            "prefill_small_m": small,
-            "w4a4_gemm_speedup_vs_bf16": (
-                round(sum(v["us"] for k, v in bf16_ref.items() if k.startswith("prefill/"))
-                      / (gemm_ms_step * 1e3), 3) if bf16_ref else None),
             "decode_timing": "events around the replay of a HIP graph of back-to-back launches "
                              "rotating over >600 MB of weight copies (Infinity Cache defeated)",
         },
@@ -637,35 +677,56 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(rows, pre, M):
-    """The oracle as it stands, timed on the host on a bounded sample: for each
-    prefill layer, NVFP4-quantize `rows` rows of X (with the full tensor's
-    scale) and run the oracle's fp64 W4A4 product against the layer's weights
-    (weight quantization is offline, outside the timing, as on the GPU)."""
+def _oracle_weights(nvfp4, w):
+    """The oracle's NVFP4 quantization of every weight row (row ranges on host
+    threads; each row depends only on the whole tensor's scale)."""
+    from concurrent.futures import ThreadPoolExecutor
+    n, k = w.shape
+    st = nvfp4.tensor_scale(w)
+    codes = np.empty((n, k // 2), dtype=np.uint8)
+    scales = np.empty((n, k // 16), dtype=np.uint8)
+
+    def one(r0):
+        c, s, _ = nvfp4.quantize(w[r0:r0 + 512], s_t=st)
+        codes[r0:r0 + 512], scales[r0:r0 + 512] = c, s
+    with ThreadPoolExecutor(max_workers=max(1, min(16, host_threads()))) as ex:
+        list(ex.map(one, range(0, n, 512)))
+    return codes, scales, st
+
+
+def cpu_baseline(rows, cfg, M):
+    """The oracle as it stands, timed on the host on a bounded sample of the
+    headline workload.  For each of the four layers (weights quantized by the
+    oracle beforehand, outside the timing: they are offline, as on the GPU):
+    the tensor scale over the whole [M, K] activation (the method's first
+    step), the NVFP4 quantization of the first `rows` token rows with that
+    scale, and the fp64 W4A4 product of those rows with the layer's weights.
+    value = 2 * rows * sum(N K) / the timed seconds."""
     sys.path.insert(0, ROOT)
     from oracle import nvfp4, gemm
-    from decode_nvfp4_rtn_amd import synth
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    prep = []
-    for li, L in enumerate(pre.layers):
-        xb = synth.activations_bf16(pre.cid, li, rows, L.k, outliers=pre.outliers)
-        w = synth.weights(pre.cid, li, L.n, L.k)
-        prep.append((L, synth.bf16_bits_as_f32(xb), nvfp4.quantize(w)))
-    t0 = time.perf_counter()
-    flops = 0.0
-    for L, x, wq in prep:
-        aq = nvfp4.quantize(x)
+        blas = None
+    cores = host_threads()
+    dt, flops = 0.0, 0.0
+    for li, L in enumerate(cfg.layers):
+        wq = _oracle_weights(nvfp4, draw_weights(cfg.cid, li, L.n, L.k))
+        xf = (draw_activations_bf16(cfg.cid, li, M, L.k, cfg.outliers).astype(np.uint32)
+              << 16).view(np.float32)
+        t0 = time.perf_counter()
+        st = nvfp4.tensor_scale(xf)
+        aq = nvfp4.quantize(xf[:rows], s_t=st)
         gemm.w4a4(*aq, *wq)
+        dt += time.perf_counter() - t0
         flops += 2.0 * rows * L.n * L.k
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{rows} of the {M} token rows of each of the 4 prefill layers "
-                      f"(quantize + fp64 product); {dt:.1f} s"}
+        del xf, wq
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "blas_threads": blas, "kind": "oracle",
+            "sample": f"the first {rows} of the {M} token rows of each of the 4 27B-class "
+                      f"layers: tensor scale over all {M} rows, quantize of the sample, fp64 "
+                      f"product; {dt:.1f} s of host time"}
 
 
 if __name__ == "__main__":
