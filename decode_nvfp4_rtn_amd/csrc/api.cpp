@@ -77,6 +77,28 @@ int quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8
                                              as_stream(stream)));
 }
 
+int quantize_nvfp4_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                           uint8_t* codes, uint8_t* scales, float* tensor_scale, unsigned flags,
+                           void* stream) {
+  if (rows < 0 || cols < 0) return QL_EINVAL;
+  if (flags & ~QL_STATIC_SCALE) return QL_EINVAL;
+  if (x_dtype != QL_F32 && x_dtype != QL_BF16) return QL_EDTYPE;
+  if (cols % 16 != 0) return QL_ESHAPE;
+  if (rows > 0 && cols > (int64_t(1) << 40) / rows) return QL_ESHAPE;
+  if (rows == 0 || cols == 0) return QL_OK;
+  if (!x || !codes || !scales || !tensor_scale) return QL_EINVAL;
+  if (!aligned16(x) || !aligned16(codes)) return QL_EALIGN;
+  const bool stat = (flags & QL_STATIC_SCALE) != 0;
+  uint32_t* partial = nullptr;
+  if (!stat) {
+    if (quantize_blocks(rows, cols) > quantize_scratch_partials()) return QL_EWORKSPACE;
+    partial = quantize_scratch();
+    if (!partial) return QL_EHIP;
+  }
+  return launch_status(launch_quantize_nvfp4(x, x_dtype, rows, cols, codes, scales,
+                                             tensor_scale, stat, partial, as_stream(stream)));
+}
+
 int quantize_int4_g128(const float* w, int64_t n, int64_t k, uint8_t* codes, uint16_t* scales,
                        void* stream) {
   if (n < 0 || k < 0) return QL_EINVAL;

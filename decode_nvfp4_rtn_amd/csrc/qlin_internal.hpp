@@ -134,6 +134,9 @@ inline BlobLayout blob_layout(int fmt, int64_t n, int64_t k) {
 // and return the hipError_t of the launch.
 // ---------------------------------------------------------------------------
 int quantize_blocks(int64_t rows, int64_t cols);
+// quantize_nvfp4_noalloc: partial maxima in a library-held array per GPU.
+int quantize_scratch_partials();
+uint32_t* quantize_scratch();
 hipError_t launch_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                  bool static_scale, uint32_t* partial, hipStream_t s);

@@ -22,12 +22,22 @@
 // division and no multiply is fused into an add.
 #include "qlin_internal.hpp"
 
+#include <mutex>
+
 namespace qlin {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxPartials = 1024;
 constexpr int kMaxEncodeBlocks = 2048;
+
+// Partial maxima of quantize_nvfp4_noalloc, the entry point for callers that
+// cannot allocate: one array in each GPU's memory for the life of the process
+// (4 KiB, kMaxPartials uint32, enough for the amax pass of any input, which
+// never runs more than kMaxPartials blocks).  In host code `scratch` names a
+// host-side stand-in, never a device address: the launcher passes the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint32_t scratch[kMaxPartials];
 
 // |x| as a binary32 bit pattern, for the two input dtypes.
 __device__ __forceinline__ uint32_t abs_bits_bf16_pair(uint32_t w, uint32_t cur) {
@@ -223,6 +233,30 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(
 }
 
 }  // namespace
+
+int quantize_scratch_partials() { return kMaxPartials; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails
+// (then it is tried again on the next call).  Host threads may call
+// concurrently: the lookup runs under a lock, the kept addresses are atomics.
+uint32_t* quantize_scratch() {
+  static std::atomic<uint32_t*> addr[64];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  uint32_t* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    p = static_cast<uint32_t*>(q);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 int quantize_blocks(int64_t rows, int64_t cols) {
   const int64_t vec = rows * cols / 8;  // 16-byte vectors of a bf16 tensor

@@ -34,6 +34,7 @@ _SIGS = {
     "ql_version": (_int, []),
     "quantize_nvfp4_workspace": (_sz, [_i64, _i64]),
     "quantize_nvfp4": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _uint, _vp, _sz, _vp]),
+    "quantize_nvfp4_noalloc": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _uint, _vp]),
     "quantize_int4_g128": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "quantize_int4_g128_sp24": (_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "fit_lut2_workspace": (_sz, [_i64, _i64]),
@@ -150,6 +151,29 @@ def quantize_nvfp4(x, tensor_scale=None, codes=None, scales=None, workspace=None
         _ptr(x), dt, rows, cols, _ptr(codes), _ptr(scales), _ptr(ts), flags,
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
     return codes, scales, ts
+
+
+def quantize_nvfp4_noalloc(x, codes, scales, tensor_scale, static_scale=False, stream=None):
+    """quantize_nvfp4 without a workspace (the library keeps the partial maxima
+    in a per-GPU array), for callers that cannot allocate: every output is the
+    caller's.  tensor_scale (1-element fp32 GPU tensor) receives s_t, or holds
+    a calibrated s_t when static_scale.  Calls that may overlap on one GPU
+    (different streams without ordering) race on that array.
+    Returns (codes, scales, tensor_scale)."""
+    _dev(x, "x")
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D, got {x.dim()}-D")
+    rows, cols = x.shape
+    dt = {torch.float32: QL_F32, torch.bfloat16: QL_BF16}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be float32 or bfloat16")
+    _bytes(codes, "codes", rows * (cols // 2), torch.uint8)
+    _bytes(scales, "scales", rows * (cols // 16), torch.uint8)
+    _bytes(tensor_scale, "tensor_scale", 4, torch.float32)
+    _check("quantize_nvfp4_noalloc", _lib.quantize_nvfp4_noalloc(
+        _ptr(x), dt, rows, cols, _ptr(codes), _ptr(scales), _ptr(tensor_scale),
+        QL_STATIC_SCALE if static_scale else 0, _stream(stream)))
+    return codes, scales, tensor_scale
 
 
 def quantize_int4_g128(w, codes=None, scales=None, stream=None, sparse24=False):

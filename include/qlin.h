@@ -98,6 +98,31 @@ int quantize_nvfp4(const void *x, int x_dtype, int64_t rows, int64_t cols,
                    void *stream);
 
 /* ------------------------------------------------------------------------
+ * quantize_nvfp4 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments, outputs and errors as quantize_nvfp4,
+ * without the workspace.  The per-block partial maxima go to a 4 KiB array
+ * (1024 x uint32) that the library keeps in each GPU's memory for the life of
+ * the process; its device address is looked up once per device, at the first
+ * call on that device (with that device current).  The call allocates and
+ * frees nothing.  Nothing in the array needs clearing: every partial a call
+ * reads is written by that call's own first pass.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that may overlap on one GPU (issued to different streams
+ * without an ordering between them) race on it and may compute a wrong
+ * tensor scale.  Calls on one stream are ordered and safe.
+ *
+ * Errors: as quantize_nvfp4 (no QL_EWORKSPACE for a missing workspace);
+ * QL_EWORKSPACE if the input would need more than 1024 partial maxima (the
+ * first pass never runs more than 1024 blocks, so no shape the other checks
+ * accept does); QL_EHIP if the array's address cannot be looked up.
+ * ---------------------------------------------------------------------- */
+int quantize_nvfp4_noalloc(const void *x, int x_dtype, int64_t rows, int64_t cols,
+                           uint8_t *codes, uint8_t *scales, float *tensor_scale,
+                           unsigned flags, void *stream);
+
+/* ------------------------------------------------------------------------
  * Symmetric INT4 weight quantization with groups of 128 along k (MARLIN
  * article, "データの扱い方": 4-bit weights, group size 128).  Per row and
  * group: a = max|w|; s = bf16(a / 7) (binary32 division, then RNE to bf16);

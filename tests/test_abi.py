@@ -32,6 +32,7 @@ def lib():
         "ql_version": (i, []),
         "quantize_nvfp4_workspace": (sz, [i64, i64]),
         "quantize_nvfp4": (i, [vp, i, i64, i64, vp, vp, vp, u, vp, sz, vp]),
+        "quantize_nvfp4_noalloc": (i, [vp, i, i64, i64, vp, vp, vp, u, vp]),
         "quantize_int4_g128": (i, [vp, i64, i64, vp, vp, vp]),
         "quantize_int4_g128_sp24": (i, [vp, i64, i64, vp, vp, vp]),
         "fit_lut2_workspace": (sz, [i64, i64]),
@@ -88,6 +89,18 @@ def test_quantize_validation(lib):
     assert q(None, 1, 0, 16, None, None, None, 0, None, 0, None) == QL_OK   # empty: no-op
     assert lib.quantize_nvfp4_workspace(0, 16) == 0
     assert lib.quantize_nvfp4_workspace(8192, 4096) >= 4
+
+
+def test_quantize_noalloc_validation(lib):
+    q = lib.quantize_nvfp4_noalloc
+    assert q(A, 1, 4, 15, B, C, D, 0, None) == QL_ESHAPE
+    assert q(A, 7, 4, 16, B, C, D, 0, None) == QL_EDTYPE
+    assert q(A, 1, 4, 16, B, C, D, 4, None) == QL_EINVAL
+    assert q(None, 1, 4, 16, B, C, D, 0, None) == QL_EINVAL
+    assert q(A, 1, 4, 16, B, C, None, 0, None) == QL_EINVAL
+    assert q(A + 4, 1, 4, 16, B, C, D, 0, None) == QL_EALIGN
+    assert q(A, 1, -1, 16, B, C, D, 0, None) == QL_EINVAL
+    assert q(None, 1, 0, 16, None, None, None, 0, None) == QL_OK   # empty: no-op
 
 
 def test_weight_prep_validation(lib):
