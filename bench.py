@@ -265,6 +265,14 @@ def main():
     M = max(big.ms)          # 32768 tokens (8192 for the Qwen3-8B-like set)
     M_DEC, M_LUT = 16, 8
 
+    def decode_ws(ws_fn, ms, L):
+        """k-split workspace of each batch size that has one (else None)."""
+        out = {}
+        for m in ms:
+            nb = ws_fn(m, L.n, L.k)
+            out[m] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        return out
+
     R = prefill_set(big, M, big.ms)
     D = []   # W4A16 decode layers
     for li, L in enumerate(dec.layers):
@@ -276,14 +284,16 @@ def main():
         del w, c, s, c24, s24
         x32 = {m: bf16(synth.decode_x_bf16(dec.cid, li, m, L.k)) for m in dec.ms}
         D.append(dict(L=L, blob=blob, blob24=blob24, x=x32,
-                      y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in dec.ms}))
+                      y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in dec.ms},
+                      ws=decode_ws(qlin.gemm_w4a16_workspace, dec.ms, L)))
     U = []   # LUT2 decode layers
     for li, L in enumerate(lut.layers):
         i, c = qlin.fit_lut2(f32(draw_weights(lut.cid, li, L.n, L.k)))
         blob = qlin.repack_weights(qlin.QL_LUT2, L.n, L.k, i, c)
         xs = {m: bf16(synth.decode_x_bf16(lut.cid, li, m, L.k)) for m in lut.ms}
         U.append(dict(L=L, blob=blob, x=xs,
-                      y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in lut.ms}))
+                      y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in lut.ms},
+                      ws=decode_ws(qlin.gemm_lut2_workspace, lut.ms, L)))
     torch.cuda.synchronize()
 
     _progress("inputs and packed weights resident")
@@ -298,9 +308,11 @@ def main():
         if ev is not None:
             ev[len(R)][0].record()
         for d in D:
-            qlin.gemm_w4a16(d["x"][M_DEC], d["blob"], d["L"].n, d["L"].k, y=d["y"][M_DEC])
+            qlin.gemm_w4a16(d["x"][M_DEC], d["blob"], d["L"].n, d["L"].k, y=d["y"][M_DEC],
+                            workspace=d["ws"][M_DEC])
         for u in U:
-            qlin.gemm_lut2(u["x"][M_LUT], u["blob"], u["L"].n, u["L"].k, y=u["y"][M_LUT])
+            qlin.gemm_lut2(u["x"][M_LUT], u["blob"], u["L"].n, u["L"].k, y=u["y"][M_LUT],
+                           workspace=u["ws"][M_LUT])
         if ev is not None:
             ev[len(R)][1].record()
 
@@ -405,13 +417,14 @@ def main():
             if m == (lut.ms if kind == "lut2" else dec.ms)[0]:
                 copies = [src.clone() for _ in range(int(np.ceil(600e6 / src.numel())))]
             x, y = rec["x"][m], rec["y"][m]
+            kw = {} if kind == "w4a16_sp24" else {"workspace": rec["ws"][m]}
             for b in copies[:3]:
-                fn(x, b, L.n, L.k, y=y)
+                fn(x, b, L.n, L.k, y=y, **kw)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for b in copies:
-                    fn(x, b, L.n, L.k, y=y)
+                    fn(x, b, L.n, L.k, y=y, **kw)
             g.replay()
             torch.cuda.synchronize()
             t = []
@@ -431,7 +444,8 @@ def main():
             _progress(f"decode {kind}/{L.name}/m{m}: {med * 1e3:.2f} us")
             rec_out = {
                 "us": round(med * 1e3, 2), "us_p10": round(p10 * 1e3, 2), "us_p90": round(p90 * 1e3, 2),
-                "gbps": round(by / med / 1e6, 1), "hbm_frac": round(by / med / 1e6 / HBM_GBPS, 3)}
+                "gbps": round(by / med / 1e6, 1), "hbm_frac": round(by / med / 1e6 / HBM_GBPS, 3),
+                "k_split": bool(kw.get("workspace") is not None)}
             if kind == "w4a16_sp24":
                 dense = sweep.get(f"w4a16/{L.name}/m{m}")
                 if dense:

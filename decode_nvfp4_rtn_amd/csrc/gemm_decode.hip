@@ -35,6 +35,10 @@
 #include "qlin_internal.hpp"
 #include "decode_ops.hpp"
 
+#include <algorithm>
+#include <climits>
+#include <type_traits>
+
 namespace qlin {
 namespace {
 
@@ -104,6 +108,77 @@ __device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (
     }
 }
 
+// Activation fragments staged as whole rows.  A fragment load (lane l: token
+// l % 16, k 32 s + 8 (l / 16)) sends adjacent lanes to different rows, which
+// the L1 cannot merge: measured with a [16, K] bf16 activation read by every
+// block, it costs 4x the L1 tag lookups and 2-2.8x the address-unit time of
+// the same bytes loaded as rows (and, with rows 24-30 KiB apart, twice the
+// time).  rows_load issues row loads instead -- lane l: token
+// m0 + 16 mt + 4 q + l / 16 (clamped to a valid row) at k 8 (l % 16) of a
+// group, for the NQ row quads that hold tokens, or with one token (NQ = 0)
+// lane l: group l / 16 -- into the registers the fragments will occupy;
+// rows_stage then sends each group through a wave-private LDS tile of 16 rows
+// x 256 bytes whose 16-byte slots are XOR-swizzled by row (conflict-free row
+// writes and fragment reads) and reads its four fragments back.  LDS
+// operations of one wave run in order, so one tile serves all the groups and
+// no barrier is needed.  Lanes of tokens past the staged rows read the last
+// staged row: their outputs are never stored.  The NG groups are
+// g0 + min(i, ng - 1), clamped to G - 1.
+__device__ __forceinline__ int stage_slot(int row, int chunk) { return row * 256 + 16 * (chunk ^ row); }
+
+template <int NG, int MT, int NQ>
+__device__ __forceinline__ void rows_load(const uint16_t* __restrict__ x, int M, int m0, int K,
+                                          int g0, int ng, int G, int lane,
+                                          bf16x8_t (&f)[NG][4][MT]) {
+  static_assert(NQ <= 4 && (NQ > 0 || (MT == 1 && NG <= 4)), "row quads");
+  auto grp = [&](int i) { return min(g0 + min(i, ng - 1), G - 1); };
+  auto ld = [](const uint16_t* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    return as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+  };
+  if constexpr (NQ == 0) {
+    f[0][0][0] = ld(x + int64_t(m0) * K + grp(lane >> 4) * 128 + 8 * (lane & 15));
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < NG; ++i)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          f[i][q][mt] = ld(x + int64_t(min(m0 + 16 * mt + 4 * q + (lane >> 4), M - 1)) * K +
+                           grp(i) * 128 + 8 * (lane & 15));
+  }
+}
+
+template <int NG, int MT, int NQ>
+__device__ __forceinline__ void rows_stage(uint8_t* st, int lane, bf16x8_t (&f)[NG][4][MT]) {
+  auto u4 = [](const bf16x8_t& v) { return __builtin_bit_cast(uint4, v); };
+  auto rd = [&](int row, int chunk) {
+    const uint4 v = *reinterpret_cast<const uint4*>(st + stage_slot(row, chunk));
+    return as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+  };
+  if constexpr (NQ == 0) {
+    *reinterpret_cast<uint4*>(st + stage_slot(lane >> 4, lane & 15)) = u4(f[0][0][0]);
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) f[i][s][0] = rd(i, 4 * s + (lane >> 4));
+  } else {
+    const int row = min(lane & 15, 4 * NQ - 1);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          *reinterpret_cast<uint4*>(st + stage_slot(4 * q + (lane >> 4), lane & 15)) =
+              u4(f[i][q][mt]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[i][s][mt] = rd(row, 4 * s + (lane >> 4));
+      }
+  }
+}
+
 // Each wave owns groups g0 .. g0 + gpw - 1 of NTB row tiles and walks them in
 // chunks of WMAX groups.  A chunk's weight loads (HBM) are issued at once;
 // activation fragments (small, L2-resident) follow one group ahead.  The
@@ -113,7 +188,10 @@ __device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (
 // fp32 scale multiply-add.  Slots past the wave's range or past k are clamped
 // to a valid address and contribute zero (their scales are replaced by 0),
 // so the loop has no branches and the compiler can count outstanding loads.
-template <int MT, int NTB, int WMAX, int KWT, bool kBF16Out>
+// XQ >= 0 (a wave's groups fit one chunk): the activation rows of all the
+// wave's groups are loaded first and staged with rows_stage (NQ = XQ) once
+// the chunk's weight loads are in flight.
+template <int MT, int NTB, int WMAX, int KWT, int XQ, bool kBF16Out>
 __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
                                                         const uint8_t* __restrict__ blob,
                                                         int64_t codes_off, int64_t sc_off, int M,
@@ -151,6 +229,10 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KWT : 1][4096];
+  bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
+  if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
+
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     uint4 wv[WMAX][NTB];
     uint2 sv[WMAX][NTB];
@@ -163,14 +245,25 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
         sv[i][nt] = sp[nt][gc * 4];
       }
     }
+    if constexpr (XQ >= 0) {
+      __builtin_amdgcn_sched_barrier(0);   // the weight loads go out before the staging
+      rows_stage<WMAX, MT, XQ>(xst[wave], lane, xpre);
+    }
     // phase 1: MFMA chains of every group of the chunk
     floatx4 acc[WMAX][NTB][MT];
     XFrag<MT> xf;
-    load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
+    if constexpr (XQ < 0) load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
       XFrag<MT> xn;
-      if (i + 1 < WMAX) load_xfrag<MT>(xn, xr, min(g0 + c0 + i + 1, G - 1));   // compile-time
+      if constexpr (XQ >= 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) xf.f[s][mt] = xpre[i][s][mt];
+      } else if (i + 1 < WMAX) {
+        load_xfrag<MT>(xn, xr, min(g0 + c0 + i + 1, G - 1));   // compile-time
+      }
       floatx4 xs[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -193,7 +286,9 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xf.f[s][mt], acc[i][nt][mt], 0, 0, 0);
         }
       }
-      if (i + 1 < WMAX) xf = xn;
+      if constexpr (XQ < 0) {
+        if (i + 1 < WMAX) xf = xn;
+      }
     }
     // phase 2: tot += group scale * (sum x q), in fp32, per group
 #pragma unroll
@@ -215,7 +310,7 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
   reduce_store<MT, NTB, KWT, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
-template <int MT, int NTB, int WMAX, int KWT, bool kBF16Out>
+template <int MT, int NTB, int WMAX, int KWT, int XQ, bool kBF16Out>
 __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ blob,
                                                        int64_t codes_off, int64_t book_off, int M,
@@ -254,6 +349,10 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) tot2[e][nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KWT : 1][4096];
+  bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
+  if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
+
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     uint2 wv[WMAX][NTB];
 #pragma unroll
@@ -262,13 +361,24 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) wv[i][nt] = load_nt8(wp[nt] + gc * 64);
     }
+    if constexpr (XQ >= 0) {
+      __builtin_amdgcn_sched_barrier(0);   // the weight loads go out before the staging
+      rows_stage<WMAX, MT, XQ>(xst[wave], lane, xpre);
+    }
     XFrag<MT> xf;
-    load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
+    if constexpr (XQ < 0) load_xfrag<MT>(xf, xr, min(g0 + c0, G - 1));
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
       const int g = g0 + c0 + i;
       XFrag<MT> xn;
-      if (i + 1 < WMAX) load_xfrag<MT>(xn, xr, min(g + 1, G - 1));   // compile-time condition
+      if constexpr (XQ >= 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) xf.f[s][mt] = xpre[i][s][mt];
+      } else if (i + 1 < WMAX) {
+        load_xfrag<MT>(xn, xr, min(g + 1, G - 1));   // compile-time condition
+      }
       const uint32_t keep = (c0 + i < gpw && g < G) ? 0xFFFFFFFFu : 0u;  // else zero codebook
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) {
@@ -283,7 +393,9 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
             tot2[i & 1][nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 a[s], xf.f[s][mt], tot2[i & 1][nt][mt], 0, 0, 0);
       }
-      if (i + 1 < WMAX) xf = xn;
+      if constexpr (XQ < 0) {
+        if (i + 1 < WMAX) xf = xn;
+      }
     }
   }
   floatx4 tot[NTB][MT];
@@ -298,28 +410,57 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
 // two chunks of W groups per wave): a block of 8 waves owns one row tile and
 // the waves split k, as above, but each wave walks its groups in chunks of W
 // with the next chunk's loads in flight while it computes the current one
-// (two register sets).  A chunk's activation fragments travel in the same
-// batch as its weights: loads complete in issue order for the wait counter,
-// so fragments fetched later would make the arithmetic wait for the next
-// chunk's weights as well.
-template <int W, bool kLut>
+// (two register sets).  A chunk's activation rows travel in the same batch
+// as its weights: loads complete in issue order for the wait counter, so
+// rows fetched later would make the arithmetic wait for the next chunk's
+// weights as well.
+//
+// Activations are loaded as whole rows and turned into MFMA fragments in LDS.
+// A fragment load (lane l: token l % 16, k 32 s + 8 (l / 16)) sends adjacent
+// lanes to different rows, so the L1 cannot merge them: measured with rows
+// 24-30 KiB apart (K = 12288, 15360), fragment loads cost 4x the L1 tag
+// lookups and 2.5-2.8x the address-unit time of the same bytes loaded as
+// rows, and twice the time.  Here lane l loads token 4 q + l / 16 at k
+// 8 (l % 16) of a group (row quad q: 256 contiguous bytes per token), only
+// the NQ quads that hold tokens < M, writes them to a wave-private LDS tile
+// [4 NQ tokens][128 k] (rows padded to 272 bytes) and reads the fragments
+// back, lanes of tokens >= 4 NQ reading the last staged row (its outputs are
+// not stored).  With one token (NQ = 0) a single load brings the chunk's four
+// groups (lane l: group l / 16).  The INT4 group scales of a chunk's four
+// groups (4 x 32 contiguous bytes) also come with one load (lane l: group
+// (l / 2) % 4, half l % 2) and reach their lanes through LDS.  LDS
+// operations of one wave run in order, so none of this needs a barrier.
+constexpr int kXRow = 272;               // LDS bytes per staged token row
+
+template <int NQ>
+constexpr int pipe_xrows() { return NQ == 0 ? 1 : 4 * NQ; }
+// LDS bytes of one wave: activation tiles (two groups' tiles, or with one
+// token the four groups of a chunk) and the chunk's scales
+template <int NQ>
+constexpr int pipe_xbytes() { return NQ == 0 ? 4 * kXRow : 2 * 4 * NQ * kXRow; }
+constexpr int kSBytes = 128;
+
+template <int W, bool kLut, int NQ>
 struct PipeBatch;
-template <int W>
-struct PipeBatch<W, false> {
+template <int W, int NQ>
+struct PipeBatch<W, false, NQ> {
   uint4 w[W];
-  uint2 s[W];
-  bf16x8_t x[W][4];
+  uint4 s;
+  uint4 x[NQ == 0 ? 1 : W][NQ == 0 ? 1 : NQ];
 };
-template <int W>
-struct PipeBatch<W, true> {
+template <int W, int NQ>
+struct PipeBatch<W, true, NQ> {
   uint2 w[W];
-  bf16x8_t x[W][4];
+  uint4 x[NQ == 0 ? 1 : W][NQ == 0 ? 1 : NQ];
 };
 
-template <int W, bool kLut, bool kBF16Out>
+template <int W, bool kLut, int NQ, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob, int64_t codes_off,
     int64_t aux_off, int M, int N, int K, void* __restrict__ y) {
+  static_assert(W == 4, "a chunk is four groups: one scale load, one single-token row load");
+  __shared__ __attribute__((aligned(16))) uint8_t xt[KW][pipe_xbytes<NQ>()];
+  __shared__ __attribute__((aligned(16))) uint8_t st[KW][kSBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
@@ -329,65 +470,115 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
   const uint32_t m136 = vconst(0xC308C308u);
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
-  const uint16_t* xr = x + int64_t(min(lane & 15, M - 1)) * K + 8 * (lane >> 4);
+  // this lane's token of each row quad (clamped to a valid row) and k offset
+  constexpr int NQR = NQ == 0 ? 1 : NQ;
+  const uint16_t* xq[NQR];
+#pragma unroll
+  for (int q = 0; q < NQR; ++q)
+    xq[q] = x + int64_t(NQ == 0 ? 0 : min(4 * q + (lane >> 4), M - 1)) * K + 8 * (lane & 15);
   uint32_t lo_t = 0, hi_t = 0;
   if constexpr (kLut) {
     const uint2 b = reinterpret_cast<const uint2*>(blob + aux_off)[tile * 16 + (lane & 15)];
     lo_t = b.x;
     hi_t = b.y;
   }
+  auto gclamp = [&](int c0, int i) { return min(g0 + min(c0 + i, gpw - 1), G - 1); };
 
-  auto load = [&](PipeBatch<W, kLut>& B, int c0) {
+  auto load = [&](PipeBatch<W, kLut, NQ>& B, int c0) {
 #pragma unroll
     for (int i = 0; i < W; ++i) {
-      const int gc = min(g0 + min(c0 + i, gpw - 1), G - 1);
-      const int64_t gi = tile * G + gc;
-      if constexpr (kLut) {
+      const int64_t gi = tile * G + gclamp(c0, i);
+      if constexpr (kLut)
         B.w[i] = load_nt8(reinterpret_cast<const uint2*>(blob + codes_off) + gi * 64 + lane);
-      } else {
+      else
         B.w[i] = load_nt16(reinterpret_cast<const uint4*>(blob + codes_off) + gi * 64 + lane);
-        B.s[i] = reinterpret_cast<const uint2*>(blob + aux_off)[gi * 4 + (lane >> 4)];
-      }
+    }
+    if constexpr (!kLut) {
+      const int64_t gs = tile * G + gclamp(c0, (lane >> 1) & 3);
+      B.s = *reinterpret_cast<const uint4*>(blob + aux_off + gs * 32 + 16 * (lane & 1));
+    }
+    if constexpr (NQ == 0) {
+      B.x[0][0] = *reinterpret_cast<const uint4*>(xq[0] + gclamp(c0, lane >> 4) * 128);
+    } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
-        B.x[i][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
-      }
+      for (int i = 0; i < W; ++i)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          B.x[i][q] = *reinterpret_cast<const uint4*>(xq[q] + gclamp(c0, i) * 128);
+    }
+  };
+
+  uint8_t* const xw = xt[wave];
+  // a chunk's shared stores (single-token rows, scales) before its groups
+  auto stage = [&](const PipeBatch<W, kLut, NQ>& B) {
+    if constexpr (NQ == 0)
+      *reinterpret_cast<uint4*>(xw + (lane >> 4) * kXRow + 16 * (lane & 15)) = B.x[0][0];
+    if constexpr (!kLut) {
+      if (lane < 8) *reinterpret_cast<uint4*>(st[wave] + 16 * lane) = B.s;
+    }
+  };
+  // fragments of group i of the chunk
+  auto fragments = [&](const PipeBatch<W, kLut, NQ>& B, int i, bf16x8_t (&f)[4]) {
+    const uint8_t* t;
+    int row;
+    if constexpr (NQ == 0) {
+      t = xw + i * kXRow;
+      row = 0;
+    } else {
+      uint8_t* tw = xw + (i & 1) * (4 * NQ * kXRow);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        *reinterpret_cast<uint4*>(tw + (4 * q + (lane >> 4)) * kXRow + 16 * (lane & 15)) =
+            B.x[i][q];
+      t = tw;
+      row = min(lane & 15, 4 * NQ - 1);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 v = *reinterpret_cast<const uint4*>(t + row * kXRow + 64 * s + 16 * (lane >> 4));
+      f[s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
     }
   };
 
   floatx4 tot[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-  auto compute = [&](const PipeBatch<W, kLut>& B, int c0) {
+  auto compute = [&](const PipeBatch<W, kLut, NQ>& B, int c0) {
+    stage(B);
     if constexpr (kLut) {
 #pragma unroll
       for (int i = 0; i < W; ++i) {
         const int g = g0 + c0 + i;
         const uint32_t keep = (c0 + i < gpw && g < G) ? 0xFFFFFFFFu : 0u;   // else zero codebook
+        bf16x8_t f[4];
+        fragments(B, i, f);
         bf16x8_t a[4];
         lut2_operands(B.w[i].x, lo_t & keep, hi_t & keep, a[0], a[1]);
         lut2_operands(B.w[i].y, lo_t & keep, hi_t & keep, a[2], a[3]);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          tot[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], B.x[i][s], tot[i & 1], 0, 0, 0);
+          tot[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], f[s], tot[i & 1], 0, 0, 0);
       }
     } else {
       floatx4 acc[W];
 #pragma unroll
       for (int i = 0; i < W; ++i) {
+        bf16x8_t f[4];
+        fragments(B, i, f);
         acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, B.x[i][s], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, f[s], acc[i], 0, 0, 0);
         const uint32_t wd[4] = {B.w[i].x, B.w[i].y, B.w[i].z, B.w[i].w};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(int4_operand(wd[s], nib_mask, bf16_128),
-                                                           B.x[i][s], acc[i], 0, 0, 0);
+                                                           f[s], acc[i], 0, 0, 0);
       }
 #pragma unroll
       for (int i = 0; i < W; ++i) {
+        // this lane's rows 4 (l / 16) .. + 3 of group i: 8 bytes of the staged scales
+        const uint2 sv = *reinterpret_cast<const uint2*>(st[wave] + 32 * i + 8 * (lane >> 4));
         const bool live = c0 + i < gpw && g0 + c0 + i < G;
-        const uint32_t s01 = live ? B.s[i].x : 0u, s23 = live ? B.s[i].y : 0u;
+        const uint32_t s01 = live ? sv.x : 0u, s23 = live ? sv.y : 0u;
         const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
                              __uint_as_float(s23 << 16), __uint_as_float(s23 & 0xFFFF0000u)};
 #pragma unroll
@@ -398,7 +589,7 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
 
   // (the scheduling barriers keep each batch's loads ahead of the arithmetic
   // on the previous one; the compiler would otherwise sink them below it)
-  PipeBatch<W, kLut> A, B;
+  PipeBatch<W, kLut, NQ> A, B;
   load(A, 0);
   int c0 = 0;
   for (; c0 + W < gpw; c0 += 2 * W) {   // chunks c0 (in A) and c0 + W (in B)
@@ -448,10 +639,10 @@ struct PersistTile<GW, true> {
 // waves per block: 8, or 16 for LUT2 with two m-tiles (two groups per wave)
 constexpr int persist_waves(int mt, bool lut) { return mt == 2 && lut ? 2 * KW : KW; }
 // Blocks of this kernel that fit on one CU: two when the registers allow four
-// waves per SIMD (one m-tile with LUT2, or INT4 with two groups per wave),
-// else one.
+// waves per SIMD (one m-tile with LUT2, or INT4 with at most three groups per
+// wave: 116 VGPRs), else one.
 constexpr int persist_blocks_per_cu(int gw, int mt, bool lut) {
-  return mt == 1 && (lut || gw == 2) ? 2 : 1;
+  return mt == 1 && (lut || gw <= 3) ? 2 : 1;
 }
 constexpr bool persist_x_in_lds(int mt, bool lut) { return mt == 2 && !lut; }
 // dynamic LDS: two reduction slots [2][waves][MT][4][64] floats, then (INT4,
@@ -459,8 +650,14 @@ constexpr bool persist_x_in_lds(int mt, bool lut) { return mt == 2 && !lut; }
 constexpr size_t persist_red_bytes(int mt, bool lut) {
   return size_t(2) * persist_waves(mt, lut) * mt * 4 * 64 * 4;
 }
+// one m-tile: the activation rows are staged through a wave-private LDS tile
+// of 16 rows x 256 bytes at the start, in the space of the reduction slots
+constexpr size_t persist_stage_bytes(int mt, bool lut) {
+  return mt == 1 ? size_t(persist_waves(mt, lut)) * 4096 : 0;
+}
 constexpr size_t persist_lds_bytes(int gw, int mt, bool lut) {
-  return persist_red_bytes(mt, lut) +
+  return (persist_red_bytes(mt, lut) > persist_stage_bytes(mt, lut)
+              ? persist_red_bytes(mt, lut) : persist_stage_bytes(mt, lut)) +
          (persist_x_in_lds(mt, lut) ? size_t(persist_waves(mt, lut)) * gw * 4 * 64 * 16 : 0);
 }
 
@@ -469,7 +666,7 @@ __global__ __launch_bounds__(persist_waves(MT, kLut) * 64,
                              persist_waves(MT, kLut) / 4 * persist_blocks_per_cu(GW, MT, kLut))
 void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                            int64_t codes_off, int64_t aux_off, int M, int N, int K,
-                           void* __restrict__ y) {
+                           void* __restrict__ y, int S, float* __restrict__ part) {
   constexpr int NW = persist_waves(MT, kLut);
   constexpr bool kXL = persist_x_in_lds(MT, kLut);
   constexpr int MR = kXL ? 1 : MT;         // m-tiles whose fragments stay in registers
@@ -480,9 +677,11 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
-  const int g0 = wave * GW;
+  // block = (tile walker, k slice): slice sl owns groups [NW GW sl, NW GW (sl + 1))
+  const int sl = blockIdx.x % S;
+  const int g0 = (sl * NW + wave) * GW;
   const int T = N / 16;
-  const int stride = gridDim.x;
+  const int stride = gridDim.x / S;   // tile walkers
   const uint32_t m136 = vconst(0xC308C308u);
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
@@ -518,26 +717,94 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
   // activation fragments (issued first), then the first tile's weights
   bf16x8_t xf[GW][4][MR];
   bf16x8_t xt[kXL ? GW : 1][4];
+  // One m-tile: the rows are loaded whole (lane l: token 4 q + l / 16 at k
+  // 8 (l % 16) of a group; with one token, lane l: group l / 16) and turned
+  // into fragments through a wave-private LDS tile [16 rows][256 B] whose
+  // 16-byte slots are XOR-swizzled by row (conflict-free writes and fragment
+  // reads).  A fragment load sends adjacent lanes to different rows, which
+  // the L1 cannot merge (4x the tag lookups of row loads).  Two m-tiles load
+  // fragments directly (their registers would not hold a row batch).
+  if constexpr (MT != 1) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 8 * (lane >> 4);
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 8 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < GW; ++i) {
-      const int gc = min(g0 + i, G - 1);
+      for (int i = 0; i < GW; ++i) {
+        const int gc = min(g0 + i, G - 1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
-        if (kXL && mt == 1)
-          xt[kXL ? i : 0][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
-        else
-          xf[i][s][mt < MR ? mt : 0] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+        for (int s = 0; s < 4; ++s) {
+          const uint4 v = *reinterpret_cast<const uint4*>(xr + gc * 128 + 32 * s);
+          if (kXL && mt == 1)
+            xt[kXL ? i : 0][s] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+          else
+            xf[i][s][mt < MR ? mt : 0] = as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
+        }
       }
     }
   }
+  uint8_t* const xstage = smem + size_t(wave) * 4096;
+  auto slot = [](int row, int chunk) { return row * 256 + 16 * (chunk ^ row); };
+  // one m-tile with NQ row quads (NQ = 0: one token): the rows are loaded
+  // into the registers their fragments will occupy, before the first tile's
+  // weights; once those are in flight each group's rows go to the LDS tile and
+  // its four fragments come back.  Every load is unconditional.
+  auto stage_rows = [&](auto nq_c, PersistTile<GW, kLut>& A0, int t0) __attribute__((always_inline)) {
+    constexpr int NQ = decltype(nq_c)::value;
+    auto as_u4 = [](const bf16x8_t& v) { return __builtin_bit_cast(uint4, v); };
+    auto as_f = [](const uint4& v) { return as_bf16x8(u32x4{v.x, v.y, v.z, v.w}); };
+    if constexpr (NQ == 0) {
+      xf[0][0][0] = as_f(*reinterpret_cast<const uint4*>(
+          x + min(g0 + (lane >> 4), G - 1) * 128 + 8 * (lane & 15)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          xf[i][q][0] = as_f(*reinterpret_cast<const uint4*>(
+              x + int64_t(min(4 * q + (lane >> 4), M - 1)) * K + min(g0 + i, G - 1) * 128 +
+              8 * (lane & 15)));
+    }
+    load(A0, t0);
+    __builtin_amdgcn_sched_barrier(0);   // keep the tile loads ahead of the staging
+    if constexpr (NQ == 0) {
+      *reinterpret_cast<uint4*>(xstage + slot(lane >> 4, lane & 15)) = as_u4(xf[0][0][0]);
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xf[i][s][0] = as_f(*reinterpret_cast<const uint4*>(xstage + slot(i, 4 * s + (lane >> 4))));
+    } else {
+      const int row = min(lane & 15, 4 * NQ - 1);   // a staged row
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          *reinterpret_cast<uint4*>(xstage + slot(4 * q + (lane >> 4), lane & 15)) =
+              as_u4(xf[i][q][0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xf[i][s][0] = as_f(*reinterpret_cast<const uint4*>(xstage + slot(row, 4 * s + (lane >> 4))));
+      }
+    }
+  };
   PersistTile<GW, kLut> A, B;
-  int t = blockIdx.x;
-  load(A, t);
-  __builtin_amdgcn_sched_barrier(0);   // keep the tile loads ahead of the seed arithmetic
+  int t = blockIdx.x / S;
+  if constexpr (MT == 1) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    if (M == 1) stage_rows(I0{}, A, t);
+    else if (M <= 4) stage_rows(I1{}, A, t);
+    else if (M <= 8) stage_rows(I2{}, A, t);
+    else if (M <= 12) stage_rows(I3{}, A, t);
+    else stage_rows(I4{}, A, t);
+    __syncthreads();   // the staging tiles share their space with the reduction slots
+  } else {
+    load(A, t);
+    __builtin_amdgcn_sched_barrier(0);   // keep the tile loads ahead of the seed arithmetic
+  }
 
   floatx4 xs[GW][MT];
   if constexpr (!kLut) {
@@ -634,7 +901,9 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
         for (int w = 0; w < h; ++w) v[w] += v[w + h];
       const int m = mt * 16 + (lane & 15), n = t * 16 + 4 * (lane >> 4) + r;
       if (m < M) {
-        if (kBF16Out)
+        if (S > 1)
+          part[(int64_t(sl) * M + m) * N + n] = v[0];   // this slice's partial sum
+        else if (kBF16Out)
           static_cast<uint16_t*>(y)[int64_t(m) * N + n] = to_bf16(v[0]);
         else
           static_cast<float*>(y)[int64_t(m) * N + n] = v[0];
@@ -642,7 +911,7 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
     }
   };
 
-  // the launch guarantees gridDim.x <= T, so every block has a first tile.
+  // the launch guarantees gridDim.x / S <= T, so every block has a first tile.
   // The second tile of an iteration may not exist (t + stride >= T): it is
   // then computed from the clamped (valid) loads but not stored.  Keeping the
   // arithmetic unconditional keeps the loop free of branches around waits,
@@ -670,27 +939,71 @@ hipError_t persist_lds_attr() {
                         int(persist_lds_bytes(GW, MT, kLut)));
 }
 
-template <bool kLut, int MT, int NTB, int WMAX, int KWT>
-hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L, int M, int m0,
-                         int N, int K, void* y, int y_dtype, hipStream_t s) {
+// Sum of the k slices' fp32 partial sums, in slice order: y = part[0] + ...
+// + part[S-1] (deterministic), four outputs per thread.
+template <bool kBF16Out>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part, int S,
+                                                            int64_t n4, void* __restrict__ y) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const floatx4* p = reinterpret_cast<const floatx4*>(part);
+  floatx4 v = p[i];
+  for (int j = 1; j < S; ++j) v += p[int64_t(j) * n4 + i];
+  if (kBF16Out) {
+    uint2 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    reinterpret_cast<uint2*>(y)[i] = o;
+  } else {
+    reinterpret_cast<floatx4*>(y)[i] = v;
+  }
+}
+
+template <bool kLut, int MT, int NTB, int WMAX, int KWT, int XQ>
+hipError_t launch_decode_xq(const void* x, const uint8_t* blob, const BlobLayout& L, int M,
+                            int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int blocks = (N / 16 + NTB - 1) / NTB;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   if constexpr (kLut) {
     if (y_dtype == 1)
-      lut2_kernel<MT, NTB, WMAX, KWT, true><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
-                                                                  L.aux_off, M, m0, N, K, y);
+      lut2_kernel<MT, NTB, WMAX, KWT, XQ, true><<<blocks, KWT * 64, 0, s>>>(
+          xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
     else
-      lut2_kernel<MT, NTB, WMAX, KWT, false><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
-                                                                   L.aux_off, M, m0, N, K, y);
+      lut2_kernel<MT, NTB, WMAX, KWT, XQ, false><<<blocks, KWT * 64, 0, s>>>(
+          xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
   } else {
     if (y_dtype == 1)
-      w4a16_kernel<MT, NTB, WMAX, KWT, true><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
-                                                                   L.aux_off, M, m0, N, K, y);
+      w4a16_kernel<MT, NTB, WMAX, KWT, XQ, true><<<blocks, KWT * 64, 0, s>>>(
+          xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
     else
-      w4a16_kernel<MT, NTB, WMAX, KWT, false><<<blocks, KWT * 64, 0, s>>>(xp, blob, L.codes_off,
-                                                                    L.aux_off, M, m0, N, K, y);
+      w4a16_kernel<MT, NTB, WMAX, KWT, XQ, false><<<blocks, KWT * 64, 0, s>>>(
+          xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
   }
   return hipGetLastError();
+}
+
+// A wave's groups in one chunk of at most four (K <= 128 KWT WMAX): the
+// activation rows are staged once (XQ = row quads of this pass's tokens, 0
+// for a single token); otherwise fragments are loaded per group (XQ = -1).
+template <bool kLut, int MT, int NTB, int WMAX, int KWT>
+hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L, int M, int m0,
+                         int N, int K, void* y, int y_dtype, hipStream_t s) {
+  const int gpw = (K / 128 + KWT - 1) / KWT;
+  const int rows = M - m0 < 16 * MT ? M - m0 : 16 * MT;
+  if constexpr (WMAX <= 4) {
+    if (gpw <= WMAX) {
+      if constexpr (MT == 1) {
+        if (rows == 1)
+          return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        if (rows <= 4)
+          return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        if (rows <= 8)
+          return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      }
+      return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    }
+  }
+  return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, -1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
 }
 
 // Largest chunk whose weight registers fit without spilling (the INT4 operand
@@ -718,9 +1031,52 @@ hipError_t launch_decode_w(const void* x, const uint8_t* blob, const BlobLayout&
   }
 }
 
+}  // namespace
+
+// Plan of the k-sliced persistent kernel: GW groups per wave, S k slices of
+// NW GW groups, P tile walkers per slice (S P blocks).  S == 0: no plan.
+DecodeSplit decode_split_plan(bool lut, int64_t m, int64_t n, int64_t k) {
+  DecodeSplit best{0, 0, 0, 0};
+  const int cus = device_cu_count();
+  if (m < 1 || m > 32 || cus <= 0 || n % 16 != 0 || k % 128 != 0) return best;
+  const int64_t T = n / 16, G = k / 128;
+  const int mt = m > 16 ? 2 : 1;
+  const int nw = persist_waves(mt, lut);
+  // Measured against the unsplit kernels (graph replay over rotating weight
+  // copies, Qwen3-8B-like and Gemma3-like decode shapes): the split pays only
+  // where k is long and the batch large enough that every block loading the
+  // whole activation dominates -- W4A16 4096 x 12288 at M = 16 1.04x, M = 32
+  // 1.66x; LUT2 3840 x 15360 at M = 16 1.09x -- and costs 0.6-0.9x at M <= 8
+  // and on K <= 4096 (the second launch adds ~1.7 us).
+  if (G <= KW * 4 || m <= 8) return best;
+  int64_t best_cost = INT64_MAX;
+  for (int gw = 1; gw <= 4; ++gw) {
+    if (mt == 2 && lut && gw > 2) break;
+    const int64_t S = (G + nw * gw - 1) / (nw * gw);
+    if (S < 2) continue;
+    const int bpc = persist_blocks_per_cu(gw, mt, lut);
+    const int64_t P = std::min<int64_t>(T, int64_t(bpc) * cus / S);
+    if (P < 1) continue;
+    // (row tile, group) units per CU, plus a round trip per pair of tiles
+    const int64_t tiles = (T + P - 1) / P;
+    const int64_t cost = tiles * nw * gw * bpc + 32 * ((tiles + 1) / 2);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = DecodeSplit{gw, mt, int(S), int(P)};
+    }
+  }
+  return best;
+}
+
+size_t decode_split_bytes(const DecodeSplit& p, int64_t m, int64_t n) {
+  return p.S < 2 ? 0 : size_t(p.S) * size_t(m) * size_t(n) * sizeof(float);
+}
+
+namespace {
+
 template <bool kLut>
 hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int64_t n, int64_t k,
-                             void* y, int y_dtype, hipStream_t s) {
+                             void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {
   const BlobLayout L = blob_layout(kLut ? 2 : 1, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
   // two row tiles per block when there are enough tiles to keep every CU busy
@@ -728,26 +1084,63 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
   const bool wide = n / 16 >= 384;
   const int G = static_cast<int>(k / 128);
   const int cus = device_cu_count();
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  auto run = [&](auto kern, int waves, int grid, size_t lds, hipError_t attr, int S,
+                 float* part) {
+    if (attr != hipSuccess) return attr;
+    kern<<<grid, waves * 64, lds, s>>>(xp, blob, L.codes_off, L.aux_off, int(m), int(n),
+                                       int(k), y, S, part);
+    return hipGetLastError();
+  };
+#define QL_PERSIST_RUN(GW, MT, GRID, S, PART)                                                \
+  (y_dtype == 1                                                                             \
+       ? run(decode_persist_kernel<GW, MT, kLut, true>, persist_waves(MT, kLut), GRID,       \
+             persist_lds_bytes(GW, MT, kLut), persist_lds_attr<GW, MT, kLut, true>(), S, PART) \
+       : run(decode_persist_kernel<GW, MT, kLut, false>, persist_waves(MT, kLut), GRID,      \
+             persist_lds_bytes(GW, MT, kLut), persist_lds_attr<GW, MT, kLut, false>(), S, PART))
+  // k-sliced persistent kernel with the caller's workspace: each block owns
+  // one k slice of several row tiles, so its activation fragments serve all
+  // of them; the slices' fp32 partial sums are added by a second launch
+  const DecodeSplit sp = decode_split_plan(kLut, m, n, k);
+  if (sp.S >= 2 && ws != nullptr && ws_bytes >= decode_split_bytes(sp, m, n)) {
+    float* part = static_cast<float*>(ws);
+    const int grid = sp.S * sp.P;
+    hipError_t e = hipSuccess;
+    if (sp.mt == 1) {
+      switch (sp.gw) {
+        case 1: e = QL_PERSIST_RUN(1, 1, grid, sp.S, part); break;
+        case 2: e = QL_PERSIST_RUN(2, 1, grid, sp.S, part); break;
+        case 3: e = QL_PERSIST_RUN(3, 1, grid, sp.S, part); break;
+        default: e = QL_PERSIST_RUN(4, 1, grid, sp.S, part); break;
+      }
+    } else if constexpr (kLut) {
+      e = sp.gw == 1 ? QL_PERSIST_RUN(1, 2, grid, sp.S, part)
+                     : QL_PERSIST_RUN(2, 2, grid, sp.S, part);
+    } else {
+      switch (sp.gw) {
+        case 1: e = QL_PERSIST_RUN(1, 2, grid, sp.S, part); break;
+        case 2: e = QL_PERSIST_RUN(2, 2, grid, sp.S, part); break;
+        case 3: e = QL_PERSIST_RUN(3, 2, grid, sp.S, part); break;
+        default: e = QL_PERSIST_RUN(4, 2, grid, sp.S, part); break;
+      }
+    }
+    if (e != hipSuccess) return e;
+    const int64_t n4 = m * n / 4;
+    const int rb = int((n4 + 255) / 256);
+    if (y_dtype == 1)
+      decode_reduce_kernel<true><<<rb, 256, 0, s>>>(part, sp.S, n4, y);
+    else
+      decode_reduce_kernel<false><<<rb, 256, 0, s>>>(part, sp.S, n4, y);
+    return hipGetLastError();
+  }
   // one pass over the batch (M <= 32), K <= 4096 and at least two row tiles
   // per CU: persistent kernel
   if (m <= 32 && G <= KW * 4 && cus > 0 && n / 16 >= 2 * cus) {
-    const uint16_t* xp = static_cast<const uint16_t*>(x);
-    const int M = int(m), N = int(n), K = int(k), T = int(n / 16);
-    auto run = [&](auto kern, int waves, int per_cu, size_t lds, hipError_t attr) {
-      if (attr != hipSuccess) return attr;
-      // every block must own at least two tiles, and the grid never exceeds T
-      const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
-      kern<<<grid, waves * 64, lds, s>>>(xp, blob, L.codes_off, L.aux_off, M, N, K, y);
-      return hipGetLastError();
-    };
-#define QL_PERSIST(GW, MT)                                                                   \
-    return y_dtype == 1                                                                     \
-               ? run(decode_persist_kernel<GW, MT, kLut, true>, persist_waves(MT, kLut),     \
-                     persist_blocks_per_cu(GW, MT, kLut), persist_lds_bytes(GW, MT, kLut),   \
-                     persist_lds_attr<GW, MT, kLut, true>())                                 \
-               : run(decode_persist_kernel<GW, MT, kLut, false>, persist_waves(MT, kLut),    \
-                     persist_blocks_per_cu(GW, MT, kLut), persist_lds_bytes(GW, MT, kLut),   \
-                     persist_lds_attr<GW, MT, kLut, false>())
+    const int T = int(n / 16);
+    // every block must own at least two tiles, and the grid never exceeds T
+    auto grid_of = [&](int per_cu) { return T >= 2 * per_cu * cus ? per_cu * cus : cus; };
+#define QL_PERSIST(GW, MT) \
+    return QL_PERSIST_RUN(GW, MT, grid_of(persist_blocks_per_cu(GW, MT, kLut)), 1, nullptr)
     if (m > 16) {
       if constexpr (kLut) {
         QL_PERSIST(2, 2);   // 16 waves: two groups per wave cover K <= 4096
@@ -762,28 +1155,33 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
     QL_PERSIST(4, 1);
 #undef QL_PERSIST
   }
+#undef QL_PERSIST_RUN
   // one m-tile, one row tile per block and long K: pipelined k-split kernel
   const int gpw8 = (G + KW - 1) / KW;
   if (m <= 16 && !wide && gpw8 >= 8) {
     const uint16_t* xp = static_cast<const uint16_t*>(x);
     const int M = int(m), N = int(n), K = int(k), T = int(n / 16);
-    // chunks of 4 groups (LUT2: 5 when that makes three chunks, no padding)
-    const bool w5 = kLut && gpw8 > 12 && gpw8 <= 15;
-#define QL_PIPE(W)                                                                          \
+    // chunks of 4 groups
+#define QL_PIPE_NQ(W, NQ)                                                                   \
     {                                                                                      \
       if (y_dtype == 1)                                                                    \
-        decode_pipe_kernel<W, kLut, true><<<T, KW * 64, 0, s>>>(xp, blob, L.codes_off,     \
-                                                               L.aux_off, M, N, K, y);     \
+        decode_pipe_kernel<W, kLut, NQ, true><<<T, KW * 64, 0, s>>>(xp, blob, L.codes_off, \
+                                                                   L.aux_off, M, N, K, y); \
       else                                                                                 \
-        decode_pipe_kernel<W, kLut, false><<<T, KW * 64, 0, s>>>(xp, blob, L.codes_off,    \
-                                                                L.aux_off, M, N, K, y);    \
+        decode_pipe_kernel<W, kLut, NQ, false><<<T, KW * 64, 0, s>>>(xp, blob, L.codes_off,\
+                                                                    L.aux_off, M, N, K, y);\
       return hipGetLastError();                                                            \
     }
-    if constexpr (kLut) {
-      if (w5) QL_PIPE(5)
+#define QL_PIPE(W)                       \
+    {                                    \
+      if (M == 1) QL_PIPE_NQ(W, 0)       \
+      if (M <= 4) QL_PIPE_NQ(W, 1)       \
+      if (M <= 8) QL_PIPE_NQ(W, 2)       \
+      QL_PIPE_NQ(W, 4)                   \
     }
     QL_PIPE(4)
 #undef QL_PIPE
+#undef QL_PIPE_NQ
   }
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = static_cast<int>(m - m0 < 32 ? m - m0 : 32);
@@ -803,13 +1201,13 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n, int64_t k,
-                             void* y, int y_dtype, hipStream_t s) {
-  return launch_decode_all<false>(x, w_packed, m, n, k, y, y_dtype, s);
+                             void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {
+  return launch_decode_all<false>(x, w_packed, m, n, k, y, y_dtype, ws, ws_bytes, s);
 }
 
 hipError_t launch_gemm_lut2(const void* x, const void* w_packed, int64_t m, int64_t n, int64_t k,
-                            void* y, int y_dtype, hipStream_t s) {
-  return launch_decode_all<true>(x, w_packed, m, n, k, y, y_dtype, s);
+                            void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {
+  return launch_decode_all<true>(x, w_packed, m, n, k, y, y_dtype, ws, ws_bytes, s);
 }
 
 }  // namespace qlin

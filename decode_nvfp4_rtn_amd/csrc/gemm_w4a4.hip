@@ -21,10 +21,14 @@
 // Products of dequantized operands are exact in fp32; only the accumulation
 // rounds.  The ceiling of this exact formulation is the dense fp16 MFMA rate.
 //
-// Two kernels share this arithmetic.  Problems with at least 256 tiles of
-// 256 x 256 go to the block-cooperative kernel (gemm_w4a4_coop.hip), which
-// dequantizes each code once per block into fp16 LDS tiles.  Smaller problems
-// use the per-wave kernel below, whose 4x smaller tiles keep every CU busy.
+// Two kernels share this arithmetic.  The block-cooperative kernel
+// (gemm_w4a4_coop.hip) dequantizes each code once per block into fp16 LDS
+// tiles of 256 x 256; it runs every problem with m > 128 and more 256 x 256
+// tiles than half the CUs (use_coop below), and a smaller problem when the
+// caller's workspace lets its tiles be split along k and the split pays
+// (split_pays: m > 128, or k >= 8192 for problems of at most half a round).
+// Every other problem uses the per-wave kernel below, whose 4x (or, with
+// fewer 128 x 128 tiles than CUs, 16x) smaller tiles keep every CU busy.
 //
 // Tiling.  Block tile 128 (n) x 128 (m), k-step 128, four waves in 2 x 2,
 // each wave 64 x 64 = 4 x 4 MFMA tiles.  Codes and scales of both operands are

@@ -170,11 +170,23 @@ hipError_t launch_gemm_w4a4_coop(const uint8_t* a_codes, const uint8_t* a_scales
                                  const float* a_ts, const void* w_packed, int64_t m, int64_t n,
                                  int64_t k, void* y, int y_dtype, float* part, bool split,
                                  hipStream_t s);
+// Decode: the k-sliced persistent plan of the workspace entry points (S < 2:
+// no split for this shape; the plain kernels run).
+struct DecodeSplit {
+  int gw;  // groups per wave
+  int mt;  // m-tiles of 16 tokens (1 or 2)
+  int S;   // k slices
+  int P;   // tile walkers per slice
+};
+DecodeSplit decode_split_plan(bool lut, int64_t m, int64_t n, int64_t k);
+size_t decode_split_bytes(const DecodeSplit& p, int64_t m, int64_t n);
 hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n,
-                             int64_t k, void* y, int y_dtype, hipStream_t s);
+                             int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                             hipStream_t s);
 hipError_t launch_gemm_w4a16_sp24(const void* x, const void* w_packed, int64_t m, int64_t n,
                                   int64_t k, void* y, int y_dtype, hipStream_t s);
 hipError_t launch_gemm_lut2(const void* x, const void* w_packed, int64_t m, int64_t n,
-                            int64_t k, void* y, int y_dtype, hipStream_t s);
+                            int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                            hipStream_t s);
 
 }  // namespace qlin

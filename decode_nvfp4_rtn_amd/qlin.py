@@ -46,6 +46,10 @@ _SIGS = {
     "gemm_w4a4_ws": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
     "gemm_w4a16": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "gemm_lut2": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "gemm_w4a16_workspace": (_sz, [_i64, _i64, _i64]),
+    "gemm_lut2_workspace": (_sz, [_i64, _i64, _i64]),
+    "gemm_w4a16_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
+    "gemm_lut2_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
     "gemm_w4a16_sp24": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -320,26 +324,44 @@ def gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k, y=None,
     return y
 
 
-def gemm_w4a16(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
-    """W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times INT4-g128 weights^T."""
+def gemm_w4a16_workspace(m, n, k):
+    return _lib.gemm_w4a16_workspace(m, n, k)
+
+
+def gemm_lut2_workspace(m, n, k):
+    return _lib.gemm_lut2_workspace(m, n, k)
+
+
+def _decode(name, fmt, x, w_packed, n, k, y, out_dtype, stream, workspace):
     m = x.shape[0] if x.dim() == 2 else -1
     _rows(x, "x", torch.bfloat16, m, k)
-    _blob(w_packed, QL_INT4_G128, n, k)
+    _blob(w_packed, fmt, n, k)
     y, dt = _out(y, m, n, out_dtype, x.device)
-    _check("gemm_w4a16", _lib.gemm_w4a16(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
+    if workspace is None:
+        _check(name, getattr(_lib, name)(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
                                          _stream(stream)))
+    else:
+        _typed(workspace, "workspace", torch.uint8)
+        _check(name + "_ws", getattr(_lib, name + "_ws")(
+            _ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt, _ptr(workspace), workspace.numel(),
+            _stream(stream)))
     return y
 
 
-def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
-    """LUT2 decode GEMM: Y [m, n] = X bf16 [m, k] times codebook weights^T."""
-    m = x.shape[0] if x.dim() == 2 else -1
-    _rows(x, "x", torch.bfloat16, m, k)
-    _blob(w_packed, QL_LUT2, n, k)
-    y, dt = _out(y, m, n, out_dtype, x.device)
-    _check("gemm_lut2", _lib.gemm_lut2(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
-                                       _stream(stream)))
-    return y
+def gemm_w4a16(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None, workspace=None):
+    """W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times INT4-g128 weights^T.
+
+    workspace: None calls gemm_w4a16; a uint8 GPU tensor of at least
+    gemm_w4a16_workspace(m, n, k) bytes calls gemm_w4a16_ws with it (k split
+    over blocks for shapes with long k or few row tiles)."""
+    return _decode("gemm_w4a16", QL_INT4_G128, x, w_packed, n, k, y, out_dtype, stream, workspace)
+
+
+def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None, workspace=None):
+    """LUT2 decode GEMM: Y [m, n] = X bf16 [m, k] times codebook weights^T.
+
+    workspace: as gemm_w4a16 (gemm_lut2_workspace / gemm_lut2_ws)."""
+    return _decode("gemm_lut2", QL_LUT2, x, w_packed, n, k, y, out_dtype, stream, workspace)
 
 
 def gemm_w4a16_sp24(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):

@@ -265,6 +265,31 @@ int gemm_w4a16(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
                int64_t k, void *y, int y_dtype, void *stream);
 
 /* ------------------------------------------------------------------------
+ * gemm_w4a16 with a caller-provided workspace that lets the k dimension be
+ * split over blocks: each block takes one k slice of several 16-row weight
+ * tiles, so the activation fragments it loads serve all of them (without a
+ * split, narrow-n shapes run one row tile per block, and every block loads
+ * the whole activation), and a second launch adds the slices' fp32 partial
+ * sums in slice order (deterministic; results differ from gemm_w4a16's in
+ * fp32 rounding only).  Same arithmetic definition and arguments as
+ * gemm_w4a16, plus:
+ *
+ * workspace        device memory of at least gemm_w4a16_workspace(m, n, k)
+ *                  bytes, 16-byte aligned, not read before it is written;
+ *                  may be NULL (then the call is gemm_w4a16).  Calls that
+ *                  share one workspace must be ordered (same stream).
+ * gemm_w4a16_workspace returns 0 when no split applies to the shape (it
+ * applies to 8 < m <= 32 with k > 4096, where it was measured faster), and
+ * depends on the current device's compute-unit count.
+ * Errors: as gemm_w4a16, and QL_EWORKSPACE when workspace is non-NULL and
+ * smaller than gemm_w4a16_workspace(m, n, k).
+ * ---------------------------------------------------------------------- */
+size_t gemm_w4a16_workspace(int64_t m, int64_t n, int64_t k);
+int gemm_w4a16_ws(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
+                  int64_t k, void *y, int y_dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * LUT2 decode GEMV (2-bit codebook weights; KLLM article section 3 and
  * Disaggregated Quantization's LUT2 decode):
  *   Y[m,n] = sum_k x[m,k] C[n, idx[n,k]]   (fp32 accumulation)
@@ -278,6 +303,20 @@ int gemm_w4a16(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
  * ---------------------------------------------------------------------- */
 int gemm_lut2(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
               int64_t k, void *y, int y_dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * gemm_lut2 with a caller-provided workspace for a k split over blocks, as
+ * gemm_w4a16_ws: same arithmetic definition and arguments as gemm_lut2, plus
+ * the workspace (at least gemm_lut2_workspace(m, n, k) bytes, 16-byte
+ * aligned, not read before it is written; NULL makes the call gemm_lut2;
+ * calls sharing a workspace must be ordered).  gemm_lut2_workspace returns 0
+ * when no split applies.  Errors: as gemm_lut2, and QL_EWORKSPACE when the
+ * workspace is non-NULL and too small.
+ * ---------------------------------------------------------------------- */
+size_t gemm_lut2_workspace(int64_t m, int64_t n, int64_t k);
+int gemm_lut2_ws(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
+                 int64_t k, void *y, int y_dtype, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * 2:4 sparse W4A16 decode GEMV / skinny GEMM (MARLIN article, "実験と結果":

@@ -45,6 +45,10 @@ def lib():
         "gemm_w4a16": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
         "gemm_lut2": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
         "gemm_w4a16_sp24": (i, [vp, vp, i64, i64, i64, vp, i, vp]),
+        "gemm_w4a16_workspace": (sz, [i64, i64, i64]),
+        "gemm_lut2_workspace": (sz, [i64, i64, i64]),
+        "gemm_w4a16_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
+        "gemm_lut2_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -141,6 +145,18 @@ def test_decode_gemm_validation(lib, fn):
     assert g(A, B, 1, 16, 128, C + 8, 1, None) == QL_EALIGN
     assert g(A, B, -2, 16, 128, C, 1, None) == QL_EINVAL
     assert g(A, B, 0, 16, 128, C, 1, None) == QL_OK
+
+
+@pytest.mark.parametrize("fn", ["gemm_w4a16_ws", "gemm_lut2_ws"])
+def test_decode_ws_validation(lib, fn):
+    g = getattr(lib, fn)
+    assert g(A, B, 1, 20, 128, C, 1, None, 0, None) == QL_ESHAPE
+    assert g(A, B, 1, 16, 128, C, 5, None, 0, None) == QL_EDTYPE
+    assert g(None, B, 1, 16, 128, C, 1, None, 0, None) == QL_EINVAL
+    assert g(A, B, 1, 16, 128, C, 1, D + 8, 64, None) == QL_EALIGN
+    assert g(A, B, 0, 16, 128, C, 1, None, 0, None) == QL_OK
+    assert lib.gemm_w4a16_workspace(0, 4096, 12288) == 0
+    assert lib.gemm_lut2_workspace(16, 20, 15360) == 0
 
 
 def test_w4a4_validation(lib):

@@ -191,6 +191,27 @@ def test_w4a4_deterministic_and_empty():
 
 # --------------------------------------------------------------- W4A16 --
 
+def _check_decode_ws(fn, ws_fn, xb, blob, n, k, ref, need_split=False):
+    """The workspace entry point (k split over blocks where the shape has
+    one) against the oracle, fp32 and bf16 outputs, twice with the same
+    workspace (deterministic)."""
+    m = xb.shape[0]
+    nb = ws_fn(m, n, k)
+    if need_split:
+        assert nb > 0, (m, n, k)
+    if nb == 0:
+        return
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    x = dev_bf16(xb)
+    y32 = fn(x, blob, n, k, out_dtype=torch.float32, workspace=ws)
+    y16 = fn(x, blob, n, k, out_dtype=torch.bfloat16, workspace=ws)
+    y16b = fn(x, blob, n, k, out_dtype=torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y16b)
+    _check(host_f64(y32), ref, False)
+    _check(host_f64(y16), ref, True)
+
+
 def test_w4a16_tiny_decode():
     q = require_gpu()
     w = synth.weights(1, 0, 256, 512)
@@ -221,6 +242,7 @@ def test_w4a16_qwen3_decode_all_batches(li):
         ref = gemm.w4a16(xb, rc, rs)
         _check(host_f64(y32), ref, False)
         _check(host_f64(y16), ref, True)
+        _check_decode_ws(q.gemm_w4a16, q.gemm_w4a16_workspace, xb, blob, n, k, ref)
 
 
 @pytest.mark.parametrize("m", [2, 17, 33, 50, 100])
@@ -291,6 +313,7 @@ def test_lut2_gemma3_decode(li):
         ref = gemm.lut2_gemm(xb, ri, rc)
         _check(host_f64(y32), ref, False)
         _check(host_f64(y16), ref, True)
+        _check_decode_ws(q.gemm_lut2, q.gemm_lut2_workspace, xb, blob, n, k, ref)
 
 
 def test_lut2_one_hot_layout_probe_and_ragged():
@@ -346,6 +369,54 @@ def test_decode_k_chunking(fmt, n, k):
         y = fn(dev_bf16(xb), blob, n, k, out_dtype=torch.float32)
         torch.cuda.synchronize()
         _check(host_f64(y)[:, cols], ref_fn(xb, *ref_w), False)
+
+
+# --------------------------------------------- decode k split (workspace) --
+# The workspace entry points split k over blocks: S slices of NW GW groups,
+# P tile walkers per slice.  These shapes give a last slice with fewer groups
+# than the others (G not a multiple of the slice), tile counts that leave
+# some walkers a tile short (the second tile of a pair computed but not
+# stored), ragged batches of one and two m-tiles, and both formats.
+
+@pytest.mark.parametrize("fmt", ["int4", "lut2"])
+@pytest.mark.parametrize("n,k", [(4096, 12288), (272, 8320), (3840, 15360), (16 * 257, 9088),
+                                 (6160, 4224), (4096, 4096), (16 * 1031, 8192)])
+def test_decode_split_ragged(fmt, n, k):
+    q = require_gpu()
+    w = synth.weights(15, k, n, k)
+    say("decode split", fmt, n, k)
+    if fmt == "int4":
+        blob = _int4_blob(q, w)
+        ref_w = orows.int4_quantize(w)
+        fn, ws_fn, ref_fn = q.gemm_w4a16, q.gemm_w4a16_workspace, gemm.w4a16
+    else:
+        blob = _lut2_blob(q, w)
+        ref_w = orows.lut2_fit(w)
+        fn, ws_fn, ref_fn = q.gemm_lut2, q.gemm_lut2_workspace, gemm.lut2_gemm
+    del w
+    for m in (9, 13, 16, 17, 25, 32):
+        xb = synth.activations_bf16(15, m, m, k)
+        _check_decode_ws(fn, ws_fn, xb, blob, n, k, ref_fn(xb, *ref_w), need_split=k > 4096)
+
+
+def test_decode_split_workspace_sizes():
+    q = require_gpu()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # k <= 4096, batches of at most 8 and above 32 need none
+    assert q.gemm_w4a16_workspace(16, 16 * 2 * cus, 4096) == 0
+    assert q.gemm_w4a16_workspace(16, 4096, 4096) == 0
+    assert q.gemm_lut2_workspace(1, 3840, 15360) == 0
+    assert q.gemm_w4a16_workspace(8, 4096, 12288) == 0
+    assert q.gemm_w4a16_workspace(33, 4096, 12288) == 0
+    # long k with 8 < m <= 32: S slices x m x n fp32 partial sums
+    for ws_fn in (q.gemm_w4a16_workspace, q.gemm_lut2_workspace):
+        for m, n, k in ((16, 4096, 12288), (9, 3840, 15360), (32, 272, 8320)):
+            nb = ws_fn(m, n, k)
+            assert nb > 0 and nb % (4 * m * n) == 0 and 2 <= nb // (4 * m * n) <= k // 128
+    # too small a workspace is refused before any launch
+    lib = q.raw()
+    st = lib.gemm_w4a16_ws(1 << 16, 1 << 17, 16, 4096, 12288, 1 << 18, 1, 1 << 19, 16, None)
+    assert st == q.QL_EWORKSPACE
 
 
 # ----------------------------------------- persistent decode tile walk --
