@@ -108,77 +108,6 @@ __device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (
     }
 }
 
-// Activation fragments staged as whole rows.  A fragment load (lane l: token
-// l % 16, k 32 s + 8 (l / 16)) sends adjacent lanes to different rows, which
-// the L1 cannot merge: measured with a [16, K] bf16 activation read by every
-// block, it costs 4x the L1 tag lookups and 2-2.8x the address-unit time of
-// the same bytes loaded as rows (and, with rows 24-30 KiB apart, twice the
-// time).  rows_load issues row loads instead -- lane l: token
-// m0 + 16 mt + 4 q + l / 16 (clamped to a valid row) at k 8 (l % 16) of a
-// group, for the NQ row quads that hold tokens, or with one token (NQ = 0)
-// lane l: group l / 16 -- into the registers the fragments will occupy;
-// rows_stage then sends each group through a wave-private LDS tile of 16 rows
-// x 256 bytes whose 16-byte slots are XOR-swizzled by row (conflict-free row
-// writes and fragment reads) and reads its four fragments back.  LDS
-// operations of one wave run in order, so one tile serves all the groups and
-// no barrier is needed.  Lanes of tokens past the staged rows read the last
-// staged row: their outputs are never stored.  The NG groups are
-// g0 + min(i, ng - 1), clamped to G - 1.
-__device__ __forceinline__ int stage_slot(int row, int chunk) { return row * 256 + 16 * (chunk ^ row); }
-
-template <int NG, int MT, int NQ>
-__device__ __forceinline__ void rows_load(const uint16_t* __restrict__ x, int M, int m0, int K,
-                                          int g0, int ng, int G, int lane,
-                                          bf16x8_t (&f)[NG][4][MT]) {
-  static_assert(NQ <= 4 && (NQ > 0 || (MT == 1 && NG <= 4)), "row quads");
-  auto grp = [&](int i) { return min(g0 + min(i, ng - 1), G - 1); };
-  auto ld = [](const uint16_t* p) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    return as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
-  };
-  if constexpr (NQ == 0) {
-    f[0][0][0] = ld(x + int64_t(m0) * K + grp(lane >> 4) * 128 + 8 * (lane & 15));
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < NG; ++i)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          f[i][q][mt] = ld(x + int64_t(min(m0 + 16 * mt + 4 * q + (lane >> 4), M - 1)) * K +
-                           grp(i) * 128 + 8 * (lane & 15));
-  }
-}
-
-template <int NG, int MT, int NQ>
-__device__ __forceinline__ void rows_stage(uint8_t* st, int lane, bf16x8_t (&f)[NG][4][MT]) {
-  auto u4 = [](const bf16x8_t& v) { return __builtin_bit_cast(uint4, v); };
-  auto rd = [&](int row, int chunk) {
-    const uint4 v = *reinterpret_cast<const uint4*>(st + stage_slot(row, chunk));
-    return as_bf16x8(u32x4{v.x, v.y, v.z, v.w});
-  };
-  if constexpr (NQ == 0) {
-    *reinterpret_cast<uint4*>(st + stage_slot(lane >> 4, lane & 15)) = u4(f[0][0][0]);
-#pragma unroll
-    for (int i = 0; i < NG; ++i)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) f[i][s][0] = rd(i, 4 * s + (lane >> 4));
-  } else {
-    const int row = min(lane & 15, 4 * NQ - 1);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < NG; ++i) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          *reinterpret_cast<uint4*>(st + stage_slot(4 * q + (lane >> 4), lane & 15)) =
-              u4(f[i][q][mt]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) f[i][s][mt] = rd(row, 4 * s + (lane >> 4));
-      }
-  }
-}
-
 // Each wave owns groups g0 .. g0 + gpw - 1 of NTB row tiles and walks them in
 // chunks of WMAX groups.  A chunk's weight loads (HBM) are issued at once;
 // activation fragments (small, L2-resident) follow one group ahead.  The
@@ -742,50 +671,16 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
       }
     }
   }
+  // one m-tile with NQ row quads (NQ = 0: one token): the rows (loaded before
+  // the first tile's weights) go through the wave's LDS staging tile once
+  // those weights are in flight
   uint8_t* const xstage = smem + size_t(wave) * 4096;
-  auto slot = [](int row, int chunk) { return row * 256 + 16 * (chunk ^ row); };
-  // one m-tile with NQ row quads (NQ = 0: one token): the rows are loaded
-  // into the registers their fragments will occupy, before the first tile's
-  // weights; once those are in flight each group's rows go to the LDS tile and
-  // its four fragments come back.  Every load is unconditional.
   auto stage_rows = [&](auto nq_c, PersistTile<GW, kLut>& A0, int t0) __attribute__((always_inline)) {
     constexpr int NQ = decltype(nq_c)::value;
-    auto as_u4 = [](const bf16x8_t& v) { return __builtin_bit_cast(uint4, v); };
-    auto as_f = [](const uint4& v) { return as_bf16x8(u32x4{v.x, v.y, v.z, v.w}); };
-    if constexpr (NQ == 0) {
-      xf[0][0][0] = as_f(*reinterpret_cast<const uint4*>(
-          x + min(g0 + (lane >> 4), G - 1) * 128 + 8 * (lane & 15)));
-    } else {
-#pragma unroll
-      for (int i = 0; i < GW; ++i)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          xf[i][q][0] = as_f(*reinterpret_cast<const uint4*>(
-              x + int64_t(min(4 * q + (lane >> 4), M - 1)) * K + min(g0 + i, G - 1) * 128 +
-              8 * (lane & 15)));
-    }
+    rows_load<GW, 1, NQ>(x, M, 0, K, g0, GW, G, lane, xf);
     load(A0, t0);
     __builtin_amdgcn_sched_barrier(0);   // keep the tile loads ahead of the staging
-    if constexpr (NQ == 0) {
-      *reinterpret_cast<uint4*>(xstage + slot(lane >> 4, lane & 15)) = as_u4(xf[0][0][0]);
-#pragma unroll
-      for (int i = 0; i < GW; ++i)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          xf[i][s][0] = as_f(*reinterpret_cast<const uint4*>(xstage + slot(i, 4 * s + (lane >> 4))));
-    } else {
-      const int row = min(lane & 15, 4 * NQ - 1);   // a staged row
-#pragma unroll
-      for (int i = 0; i < GW; ++i) {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          *reinterpret_cast<uint4*>(xstage + slot(4 * q + (lane >> 4), lane & 15)) =
-              as_u4(xf[i][q][0]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          xf[i][s][0] = as_f(*reinterpret_cast<const uint4*>(xstage + slot(row, 4 * s + (lane >> 4))));
-      }
-    }
+    rows_stage<GW, 1, NQ>(xstage, lane, xf);
   };
   PersistTile<GW, kLut> A, B;
   int t = blockIdx.x / S;

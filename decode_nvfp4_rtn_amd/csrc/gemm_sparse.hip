@@ -40,6 +40,12 @@ __device__ __forceinline__ bf16x16_t load_xh(const uint16_t* xr, int g, int s) {
   return __builtin_bit_cast(bf16x16_t, u32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w});
 }
 
+// two 8-element pieces -> one 16-element sparse-MFMA B operand
+__device__ __forceinline__ bf16x16_t join16(bf16x8_t a, bf16x8_t b) {
+  const uint4 u = __builtin_bit_cast(uint4, a), v = __builtin_bit_cast(uint4, b);
+  return __builtin_bit_cast(bf16x16_t, u32x8{u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w});
+}
+
 // codes (dword per 64-k half), positions and the 4 scales of one
 // (row tile, group) as this lane holds them
 struct SpGroup {
@@ -112,7 +118,7 @@ __device__ __forceinline__ void store_one(void* y, int64_t idx, float v) {
 // shared by the m-tiles.
 constexpr int sp_blocks_per_cu(int gw, int mt) { return gw == 2 && mt == 1 ? 2 : 1; }
 
-template <int GW, int MT, bool kBF16Out>
+template <int GW, int MT, int XQ, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64, KW / 4 * sp_blocks_per_cu(GW, MT))
 void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                          int64_t codes_off, int64_t aux_off, int M, int N, int K,
@@ -127,16 +133,6 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
 
-  bf16x16_t xh[MT][GW][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 16 * (lane >> 4);
-#pragma unroll
-    for (int i = 0; i < GW; ++i)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) xh[mt][i][s] = load_xh(xr, min(g0 + i, G - 1), s);
-  }
-
   struct Tile {
     SpGroup g[GW];
   };
@@ -145,6 +141,38 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < GW; ++i) sp_load(A.g[i], R, lane, min(g0 + i, G - 1));
   };
+
+  // activation operands: XQ >= 0 loads whole rows (XQ row quads per m-tile,
+  // 0 for one token) and stages them through a wave-private LDS tile
+  // (rows_stage, decode_ops.hpp), issued before and finished after the first
+  // tile's weight loads; XQ < 0 loads the operands directly
+  __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KW : 1][4096];
+  bf16x16_t xh[MT][GW][2];
+  Tile A, B;
+  int t = blockIdx.x;
+  if constexpr (XQ >= 0) {
+    bf16x8_t f[GW][4][MT];
+    rows_load<GW, MT, XQ>(x, M, 0, K, g0, GW, G, lane, f);
+    load(A, t);
+    __builtin_amdgcn_sched_barrier(0);
+    rows_stage<GW, MT, XQ, true>(xst[wave], lane, f);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xh[mt][i][h] = join16(f[i][2 * h][mt], f[i][2 * h + 1][mt]);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* xr = x + int64_t(min(mt * 16 + (lane & 15), M - 1)) * K + 16 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) xh[mt][i][s] = load_xh(xr, min(g0 + i, G - 1), s);
+    }
+    load(A, t);
+  }
 
   __shared__ float red[2][KW][MT][4][64];
   auto finish = [&](const Tile& A, int t, int slot, bool store) {
@@ -178,9 +206,6 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   // the launch guarantees gridDim.x <= T; the second tile of an iteration is
   // computed from clamped loads but not stored when it does not exist (no
   // branch around the waits, which would also wait for the prefetch)
-  Tile A, B;
-  int t = blockIdx.x;
-  load(A, t);
   for (; t < T; t += 2 * stride) {
     load(B, min(t + stride, T - 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -196,7 +221,7 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
 // groups in chunks of WMAX whose weight loads are issued at once; the
 // activation fragments of a group follow (small, cached).  Slots past the
 // wave's range or past k read a clamped group and contribute zero.
-template <int MT, int NTB, int WMAX, bool kBF16Out>
+template <int MT, int NTB, int WMAX, int XQ, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob, int64_t codes_off,
     int64_t aux_off, int M, int m0, int N, int K, void* __restrict__ y) {
@@ -226,6 +251,13 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // XQ >= 0 (the wave's groups fit one chunk): the activation rows of all
+  // its groups are loaded first and staged (rows_stage) once the chunk's
+  // weight loads are in flight; XQ < 0 loads each group's operands directly
+  __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KW : 1][4096];
+  bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
+  if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
+
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     SpGroup w[WMAX][NTB];
 #pragma unroll
@@ -233,6 +265,10 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
       const int gc = min(g0 + min(c0 + i, gpw - 1), G - 1);
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) sp_load(w[i][nt], R[nt], lane, gc);
+    }
+    if constexpr (XQ >= 0) {
+      __builtin_amdgcn_sched_barrier(0);   // the weight loads go out before the staging
+      rows_stage<WMAX, MT, XQ, true>(xst[wave], lane, xpre);
     }
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
@@ -242,7 +278,10 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) xh[mt][s] = load_xh(xr[mt], gc, s);
+        for (int s = 0; s < 2; ++s)
+          xh[mt][s] = XQ >= 0 ? join16(xpre[XQ >= 0 ? i : 0][2 * s][mt],
+                                       xpre[XQ >= 0 ? i : 0][2 * s + 1][mt])
+                              : load_xh(xr[mt], gc, s);
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt)
 #pragma unroll
@@ -279,43 +318,87 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
 // accumulators must fit next to the fragments at two waves per SIMD
 constexpr int sp_cap(int mt, int ntb) { return mt * ntb == 1 ? 8 : (mt * ntb == 2 ? 6 : 4); }
 
+// row quads staged for `rows` tokens of one pass: 0 for one token, else
+// 1, 2 or 4 per m-tile (-1: no staging)
+inline int stage_quads(int rows, int mt) { return mt == 2 ? 4 : rows == 1 ? 0 : rows <= 4 ? 1 : rows <= 8 ? 2 : 4; }
+
+template <int MT, int NTB, int W, int XQ>
+hipError_t launch_sp24_ksplit_xq(const uint16_t* x, const uint8_t* blob, const BlobLayout& L,
+                                 int M, int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
+  const int blocks = (N / 16 + NTB - 1) / NTB;
+  if (y_dtype == 1)
+    sp24_ksplit_kernel<MT, NTB, W, XQ, true><<<blocks, KW * 64, 0, s>>>(
+        x, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
+  else
+    sp24_ksplit_kernel<MT, NTB, W, XQ, false><<<blocks, KW * 64, 0, s>>>(
+        x, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
+  return hipGetLastError();
+}
+
+template <int MT, int NTB, int W>
+hipError_t launch_sp24_ksplit_w(const uint16_t* x, const uint8_t* blob, const BlobLayout& L,
+                                int M, int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
+  const int gpw = (K / 128 + KW - 1) / KW;
+  const int rows = M - m0 < 16 * MT ? M - m0 : 16 * MT;
+  if constexpr (W <= 4) {
+    if (gpw <= W) {
+      switch (stage_quads(rows, MT)) {
+        case 0:
+          if constexpr (MT == 1)
+            return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+          break;
+        case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      }
+    }
+  }
+  return launch_sp24_ksplit_xq<MT, NTB, W, -1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+}
+
 template <int MT, int NTB>
 hipError_t launch_sp24_ksplit(const uint16_t* x, const uint8_t* blob, const BlobLayout& L, int M,
                               int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
   constexpr int kCap = sp_cap(MT, NTB);
-  const int blocks = (N / 16 + NTB - 1) / NTB;
-#define QL_SPK(W)                                                                            \
-  {                                                                                         \
-    if (y_dtype == 1)                                                                       \
-      sp24_ksplit_kernel<MT, NTB, cmin(W, kCap), true><<<blocks, KW * 64, 0, s>>>(          \
-          x, blob, L.codes_off, L.aux_off, M, m0, N, K, y);                     \
-    else                                                                                    \
-      sp24_ksplit_kernel<MT, NTB, cmin(W, kCap), false><<<blocks, KW * 64, 0, s>>>(         \
-          x, blob, L.codes_off, L.aux_off, M, m0, N, K, y);                     \
-    return hipGetLastError();                                                               \
-  }
   switch (pick_chunk((K / 128 + KW - 1) / KW, kCap)) {
-    case 2: QL_SPK(2)
-    case 4: QL_SPK(4)
-    case 6: QL_SPK(6)
-    default: QL_SPK(8)
+    case 2: return launch_sp24_ksplit_w<MT, NTB, cmin(2, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 4: return launch_sp24_ksplit_w<MT, NTB, cmin(4, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    case 6: return launch_sp24_ksplit_w<MT, NTB, cmin(6, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    default: return launch_sp24_ksplit_w<MT, NTB, cmin(8, kCap)>(x, blob, L, M, m0, N, K, y, y_dtype, s);
   }
-#undef QL_SPK
+}
+
+template <int GW, int MT, int XQ>
+hipError_t launch_sp24_persist_xq(const uint16_t* x, const uint8_t* blob, const BlobLayout& L,
+                                  int M, int N, int K, void* y, int y_dtype, int cus,
+                                  hipStream_t s) {
+  const int T = N / 16, per_cu = sp_blocks_per_cu(GW, MT);
+  // every block owns at least two tiles, and the grid never exceeds T
+  const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
+  if (y_dtype == 1)
+    sp24_persist_kernel<GW, MT, XQ, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off,
+                                                                   L.aux_off, M, N, K, y);
+  else
+    sp24_persist_kernel<GW, MT, XQ, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off,
+                                                                    L.aux_off, M, N, K, y);
+  return hipGetLastError();
 }
 
 template <int GW, int MT>
 hipError_t launch_sp24_persist(const uint16_t* x, const uint8_t* blob, const BlobLayout& L, int M,
                                int N, int K, void* y, int y_dtype, int cus, hipStream_t s) {
-  const int T = N / 16, per_cu = sp_blocks_per_cu(GW, MT);
-  // every block owns at least two tiles, and the grid never exceeds T
-  const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
-  if (y_dtype == 1)
-    sp24_persist_kernel<GW, MT, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.aux_off,
-                                                               M, N, K, y);
-  else
-    sp24_persist_kernel<GW, MT, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off, L.aux_off,
-                                                                M, N, K, y);
-  return hipGetLastError();
+  if constexpr (MT == 2)
+    return launch_sp24_persist_xq<GW, MT, 4>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+  switch (stage_quads(M, MT)) {
+    case 0:
+      if constexpr (MT == 1)
+        return launch_sp24_persist_xq<GW, MT, 0>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+      break;
+    case 1: return launch_sp24_persist_xq<GW, MT, 1>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+    case 2: return launch_sp24_persist_xq<GW, MT, 2>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+    default: break;
+  }
+  return launch_sp24_persist_xq<GW, MT, 4>(x, blob, L, M, N, K, y, y_dtype, cus, s);
 }
 
 }  // namespace
