@@ -162,6 +162,7 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
   bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
   if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
 
+  uint32_t hdr = 0;   // header words (lane l: word l % 8)
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     uint4 wv[WMAX][NTB];
     uint2 sv[WMAX][NTB];
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
         sv[i][nt] = sp[nt][gc * 4];
       }
     }
+    if (c0 == 0) hdr = header_word(blob);   // behind the first weights; tested before the store
     if constexpr (XQ >= 0) {
       __builtin_amdgcn_sched_barrier(0);   // the weight loads go out before the staging
       rows_stage<WMAX, MT, XQ>(xst[wave], lane, xpre);
@@ -236,6 +238,7 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
       }
     }
   }
+  if (!header_word_ok(hdr, 1, N, K)) return;   // uniform: no wave reaches the barrier in reduce_store
   reduce_store<MT, NTB, KWT, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
@@ -282,6 +285,7 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
   bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
   if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
 
+  uint32_t hdr = 0;   // header words (lane l: word l % 8)
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     uint2 wv[WMAX][NTB];
 #pragma unroll
@@ -290,6 +294,7 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) wv[i][nt] = load_nt8(wp[nt] + gc * 64);
     }
+    if (c0 == 0) hdr = header_word(blob);   // behind the first weights; tested before the store
     if constexpr (XQ >= 0) {
       __builtin_amdgcn_sched_barrier(0);   // the weight loads go out before the staging
       rows_stage<WMAX, MT, XQ>(xst[wave], lane, xpre);
@@ -332,6 +337,7 @@ __global__ __launch_bounds__(KWT * 64) void lut2_kernel(const uint16_t* __restri
   for (int nt = 0; nt < NTB; ++nt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = tot2[0][nt][mt] + tot2[1][nt][mt];
+  if (!header_word_ok(hdr, 2, N, K)) return;   // uniform: no wave reaches the barrier in reduce_store
   reduce_store<MT, NTB, KWT, kBF16Out>(tot, nt0, m0, M, N, y);
 }
 
@@ -399,12 +405,18 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
   const uint32_t m136 = vconst(0xC308C308u);
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
-  // this lane's token of each row quad (clamped to a valid row) and k offset
+  // byte offset of this lane's token of each row quad (clamped to a valid
+  // row) and k position: 32 bits, added to the uniform group address
   constexpr int NQR = NQ == 0 ? 1 : NQ;
-  const uint16_t* xq[NQR];
+  uint32_t xq[NQR];
 #pragma unroll
   for (int q = 0; q < NQR; ++q)
-    xq[q] = x + int64_t(NQ == 0 ? 0 : min(4 * q + (lane >> 4), M - 1)) * K + 8 * (lane & 15);
+    xq[q] = 2u * (uint32_t(NQ == 0 ? 0 : min(4 * q + (lane >> 4), M - 1)) * uint32_t(K) +
+                  8u * uint32_t(lane & 15));
+  auto xrow = [&](int q, int g) {
+    return *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(x) + int64_t(g) * 256 +
+                                           xq[q]);
+  };
   uint32_t lo_t = 0, hi_t = 0;
   if constexpr (kLut) {
     const uint2 b = reinterpret_cast<const uint2*>(blob + aux_off)[tile * 16 + (lane & 15)];
@@ -427,13 +439,12 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
       B.s = *reinterpret_cast<const uint4*>(blob + aux_off + gs * 32 + 16 * (lane & 1));
     }
     if constexpr (NQ == 0) {
-      B.x[0][0] = *reinterpret_cast<const uint4*>(xq[0] + gclamp(c0, lane >> 4) * 128);
+      B.x[0][0] = xrow(0, gclamp(c0, lane >> 4));
     } else {
 #pragma unroll
       for (int i = 0; i < W; ++i)
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          B.x[i][q] = *reinterpret_cast<const uint4*>(xq[q] + gclamp(c0, i) * 128);
+        for (int q = 0; q < NQ; ++q) B.x[i][q] = xrow(q, gclamp(c0, i));
     }
   };
 
@@ -520,6 +531,7 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
   // on the previous one; the compiler would otherwise sink them below it)
   PipeBatch<W, kLut, NQ> A, B;
   load(A, 0);
+  const uint32_t hdr = header_word(blob);   // behind the first weights; tested before the store
   int c0 = 0;
   for (; c0 + W < gpw; c0 += 2 * W) {   // chunks c0 (in A) and c0 + W (in B)
     load(B, c0 + W);
@@ -531,6 +543,7 @@ __global__ __launch_bounds__(KW * 64) void decode_pipe_kernel(
   }
   if (c0 < gpw) compute(A, c0);          // wave-uniform: an odd last chunk
   floatx4 t1[1][1] = {{tot[0] + tot[1]}};
+  if (!header_word_ok(hdr, kLut ? 2 : 1, N, K)) return;   // uniform: no wave reaches the barrier in reduce_store
   reduce_store<1, 1, KW, kBF16Out>(t1, int(tile), 0, M, N, y);
 }
 
@@ -596,6 +609,7 @@ __global__ __launch_bounds__(persist_waves(MT, kLut) * 64,
 void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                            int64_t codes_off, int64_t aux_off, int M, int N, int K,
                            void* __restrict__ y, int S, float* __restrict__ part) {
+  const uint32_t hdr = header_word(blob);   // tested before the first store
   constexpr int NW = persist_waves(MT, kLut);
   constexpr bool kXL = persist_x_in_lds(MT, kLut);
   constexpr int MR = kXL ? 1 : MT;         // m-tiles whose fragments stay in registers
@@ -721,6 +735,9 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
 #pragma unroll
       for (int s = 0; s < 4; ++s) xl[((wave * GW + i) * 4 + s) * 64 + lane] = xt[i][s];
   }
+  // the header was loaded ahead of the activations, which the code above has
+  // waited for: tested once here, for every store below
+  const bool hdr_ok = header_word_ok(hdr, kLut ? 2 : 1, N, K);
 
   auto finish = [&](const PersistTile<GW, kLut>& A, int t, int slot, bool store) {
     floatx4 tot[MT];
@@ -785,7 +802,8 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
 #pragma unroll
       for (int r = 0; r < 4; ++r) rs[((wave * MT + mt) * 4 + r) * 64 + lane] = tot[mt][r];
     __syncthreads();
-    if (wave < 4 * MT && store) {
+    // (a blob of another format or shape is read but never stored from)
+    if (wave < 4 * MT && store && hdr_ok) {
       const int mt = wave >> 2, r = wave & 3;
       float v[NW];
 #pragma unroll
@@ -838,12 +856,20 @@ hipError_t persist_lds_attr() {
 // + part[S-1] (deterministic), four outputs per thread.
 template <bool kBF16Out>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part, int S,
-                                                            int64_t n4, void* __restrict__ y) {
+                                                            int64_t n4, void* __restrict__ y,
+                                                            const uint8_t* __restrict__ blob,
+                                                            int fmt, int N, int K) {
+  // the partial sums were not written when the blob does not match (tested
+  // before the store, as in the main kernel)
+  const uint32_t hdr = header_word(blob);   // tested before the store
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= n4) return;
   const floatx4* p = reinterpret_cast<const floatx4*>(part);
-  floatx4 v = p[i];
-  for (int j = 1; j < S; ++j) v += p[int64_t(j) * n4 + i];
+  floatx4 v = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (i < n4) {
+    v = p[i];
+    for (int j = 1; j < S; ++j) v += p[int64_t(j) * n4 + i];
+  }
+  if (!header_word_ok(hdr, fmt, N, K) || i >= n4) return;
   if (kBF16Out) {
     uint2 o;
     o.x = pack_bf16x2(v[0], v[1]);
@@ -1023,9 +1049,11 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
     const int64_t n4 = m * n / 4;
     const int rb = int((n4 + 255) / 256);
     if (y_dtype == 1)
-      decode_reduce_kernel<true><<<rb, 256, 0, s>>>(part, sp.S, n4, y);
+      decode_reduce_kernel<true><<<rb, 256, 0, s>>>(part, sp.S, n4, y, blob, kLut ? 2 : 1, int(n),
+                                                    int(k));
     else
-      decode_reduce_kernel<false><<<rb, 256, 0, s>>>(part, sp.S, n4, y);
+      decode_reduce_kernel<false><<<rb, 256, 0, s>>>(part, sp.S, n4, y, blob, kLut ? 2 : 1, int(n),
+                                                     int(k));
     return hipGetLastError();
   }
   // one pass over the batch (M <= 32), K <= 4096 and at least two row tiles

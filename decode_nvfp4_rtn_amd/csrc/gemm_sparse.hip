@@ -123,6 +123,7 @@ __global__ __launch_bounds__(KW * 64, KW / 4 * sp_blocks_per_cu(GW, MT))
 void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                          int64_t codes_off, int64_t aux_off, int M, int N, int K,
                          void* __restrict__ y) {
+  const uint32_t hdr = header_word(blob);   // tested before the first store
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
@@ -173,6 +174,9 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     }
     load(A, t);
   }
+  // the header was loaded ahead of the activations (which the staging above
+  // waits for): tested once here, for every store below
+  const bool hdr_ok = header_word_ok(hdr, 3, N, K);
 
   __shared__ float red[2][KW][MT][4][64];
   auto finish = [&](const Tile& A, int t, int slot, bool store) {
@@ -189,7 +193,8 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
       for (int r = 0; r < 4; ++r) red[slot][wave][mt][r][lane] = tot[r];
     }
     __syncthreads();
-    if (wave < 4 * MT && store) {
+    // (a blob of another format or shape is read but never stored from)
+    if (wave < 4 * MT && store && hdr_ok) {
       const int mt = wave >> 2, r = wave & 3;
       float v[KW];
 #pragma unroll
@@ -258,6 +263,7 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
   bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
   if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
 
+  uint32_t hdr = 0;   // header words (lane l: word l % 8)
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     SpGroup w[WMAX][NTB];
 #pragma unroll
@@ -266,6 +272,7 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
 #pragma unroll
       for (int nt = 0; nt < NTB; ++nt) sp_load(w[i][nt], R[nt], lane, gc);
     }
+    if (c0 == 0) hdr = header_word(blob);   // behind the first weights; tested before the store
     if constexpr (XQ >= 0) {
       __builtin_amdgcn_sched_barrier(0);   // the weight loads go out before the staging
       rows_stage<WMAX, MT, XQ, true>(xst[wave], lane, xpre);
@@ -291,6 +298,7 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
     }
   }
 
+  if (!header_word_ok(hdr, 3, N, K)) return;   // uniform: before the barrier below
   // KW partial sums -> LDS; wave c handles (row tile, m-tile, component) c, c + KW, ...
   __shared__ float red[KW][NTB][MT][4][64];
 #pragma unroll
@@ -340,16 +348,19 @@ hipError_t launch_sp24_ksplit_w(const uint16_t* x, const uint8_t* blob, const Bl
                                 int M, int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int gpw = (K / 128 + KW - 1) / KW;
   const int rows = M - m0 < 16 * MT ? M - m0 : 16 * MT;
-  if constexpr (W <= 4) {
+  // (two m-tiles of two row tiles keep per-group loads: the staged rows would
+  // not fit next to the chunk's weights)
+  if constexpr (W <= 4 && MT * NTB <= 2) {
     if (gpw <= W) {
-      switch (stage_quads(rows, MT)) {
-        case 0:
-          if constexpr (MT == 1)
-            return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-          break;
-        case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-        case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-        default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      if constexpr (MT == 2) {
+        return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      } else {
+        switch (stage_quads(rows, MT)) {
+          case 0: return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+          case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+          case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+          default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        }
       }
     }
   }

@@ -85,17 +85,49 @@ struct BlobHeader {
 static_assert(sizeof(BlobHeader) == 256, "header size");
 
 // Device-side check of a blob against the call's format and shape.  The host
-// cannot read the header without a synchronising copy, so the W4A4 kernels
-// test it first and, on a mismatch, return before any other memory access:
-// a blob packed for another format or shape is never read past its end, and
-// the output is left as it was.  The result is the same for every thread.
-// (The decode kernels do not: there the header read ahead of the first
-// weight loads measured 2-23 % slower on microsecond-long launches.)
+// cannot read the header without a synchronising copy, so the kernels test it
+// themselves; the result is the same for every thread.  Words tested: 0
+// magic, 1 version, 2 format, 4-5 n, 6-7 k (int64, little-endian; n and k of
+// a call are below 2^31).
+//
+// The W4A4 kernels test it first (one scalar load, combined without branches
+// so that no load waits for another) and, on a mismatch, return before any
+// other memory access: a blob packed for another format or shape is never
+// read past its end.
 __device__ __forceinline__ bool blob_matches(const uint8_t* blob, int fmt, int n, int k) {
-  const BlobHeader* h = reinterpret_cast<const BlobHeader*>(blob);
-  return h->magic == kBlobMagic && h->version == kBlobVersion && h->fmt == fmt && h->n == n &&
-         h->k == k;
+  const uint4* p = reinterpret_cast<const uint4*>(blob);
+  const uint4 a = p[0], b = p[1];
+  const uint32_t diff = (a.x ^ kBlobMagic) | (a.y ^ uint32_t(kBlobVersion)) | (a.z ^ uint32_t(fmt)) |
+                        (b.x ^ uint32_t(n)) | b.y | (b.z ^ uint32_t(k)) | b.w;
+  return diff == 0;
 }
+
+// The decode kernels cannot wait for the header ahead of their weights (that
+// measured 2-23 % slower on their microsecond launches).  A scalar load
+// cannot be left in flight either (scalar loads return out of order, so the
+// next wait on any scalar load or LDS access would wait for it too), nor can
+// an LDS-direct copy (the compiler then waits for every vector load before
+// each LDS access).  So lane l loads header word l % 8 with a vector load
+// issued with the first weight loads -- vector loads complete in order, so a
+// wait for anything issued after it covers it -- and header_word_ok reads
+// lanes 0-7 into scalar registers and tests them before the first store: one
+// register per lane, 0.6 % of the decode time measured over the Qwen3-8B-like
+// and Gemma3-like decode shapes.  On a mismatch the kernel stores nothing,
+// after reading the buffer as a blob of the expected format and size.
+__device__ __forceinline__ uint32_t header_word(const uint8_t* blob) {
+  return reinterpret_cast<const uint32_t*>(blob)[threadIdx.x & 7];
+}
+
+__device__ __forceinline__ bool header_word_ok(uint32_t w, int fmt, int n, int k) {
+  asm volatile("" : "+v"(w));   // tested here: the test and its wait stay at this point
+  auto word = [&](int j) { return uint32_t(__builtin_amdgcn_readlane(int(w), j)); };
+  const uint32_t diff = (word(0) ^ kBlobMagic) | (word(1) ^ uint32_t(kBlobVersion)) |
+                        (word(2) ^ uint32_t(fmt)) | (word(4) ^ uint32_t(n)) | word(5) |
+                        (word(6) ^ uint32_t(k)) | word(7);
+  return diff == 0;
+}
+
+static_assert(offsetof(BlobHeader, n) == 16 && offsetof(BlobHeader, k) == 24, "header words");
 
 // Region offsets (bytes from the start of the blob), shared by the repacker
 // and the GEMM launchers.

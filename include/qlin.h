@@ -256,10 +256,12 @@ int gemm_w4a4_ws(const uint8_t *a_codes, const uint8_t *a_scales,
  * y        out [m, n], QL_F32 or QL_BF16.
  * Tuned for m <= 32 (decode batches); any m >= 0 is accepted.
  * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
- * The blob must be one of this format packed for this (n, k): the decode
- * kernels read it without checking its header (a header read ahead of the
- * first weight loads costs 2-23 % on these microsecond launches), so any
- * other blob is read as if it were one, possibly past its end.
+ * The kernels read the blob header together with their first weight loads
+ * and test it (magic, version, format, n, k) before their first store: a blob
+ * that is not one of this format packed for this (n, k) leaves y untouched
+ * (the host cannot detect it without synchronising, so no status reports
+ * it).  It is read as a blob of this format and shape first, so the buffer
+ * must hold at least repack_weights_bytes(format, n, k) bytes.
  * ---------------------------------------------------------------------- */
 int gemm_w4a16(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
                int64_t k, void *y, int y_dtype, void *stream);
@@ -296,10 +298,12 @@ int gemm_w4a16_ws(const void *x_bf16, const void *w_packed, int64_t m, int64_t n
  * x        [m, k] bf16.   w_packed: LUT2 blob from repack_weights.
  * y        out [m, n], QL_F32 or QL_BF16.
  * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
- * The blob must be one of this format packed for this (n, k): the decode
- * kernels read it without checking its header (a header read ahead of the
- * first weight loads costs 2-23 % on these microsecond launches), so any
- * other blob is read as if it were one, possibly past its end.
+ * The kernels read the blob header together with their first weight loads
+ * and test it (magic, version, format, n, k) before their first store: a blob
+ * that is not one of this format packed for this (n, k) leaves y untouched
+ * (the host cannot detect it without synchronising, so no status reports
+ * it).  It is read as a blob of this format and shape first, so the buffer
+ * must hold at least repack_weights_bytes(format, n, k) bytes.
  * ---------------------------------------------------------------------- */
 int gemm_lut2(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
               int64_t k, void *y, int y_dtype, void *stream);
@@ -326,10 +330,12 @@ int gemm_lut2_ws(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
  * y        out [m, n], QL_F32 or QL_BF16.
  * Tuned for m <= 32; any m >= 0 is accepted.
  * Shapes: n % 16 == 0, k % 128 == 0.  Errors as gemm_w4a4.
- * The blob must be one of this format packed for this (n, k): the decode
- * kernels read it without checking its header (a header read ahead of the
- * first weight loads costs 2-23 % on these microsecond launches), so any
- * other blob is read as if it were one, possibly past its end.
+ * The kernels read the blob header together with their first weight loads
+ * and test it (magic, version, format, n, k) before their first store: a blob
+ * that is not one of this format packed for this (n, k) leaves y untouched
+ * (the host cannot detect it without synchronising, so no status reports
+ * it).  It is read as a blob of this format and shape first, so the buffer
+ * must hold at least repack_weights_bytes(format, n, k) bytes.
  * ---------------------------------------------------------------------- */
 int gemm_w4a16_sp24(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
                     int64_t k, void *y, int y_dtype, void *stream);

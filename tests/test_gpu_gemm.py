@@ -557,8 +557,7 @@ def test_w4a4_workspace_not_needed_for_whole_rounds():
 # The host cannot read a blob's header without a synchronising copy, so the
 # W4A4 kernels check it (magic, version, format, n, k) before any other access
 # and return on a mismatch: the output keeps its previous contents and no byte
-# past the blob is read.  (The decode kernels take the blob on trust; their
-# contract says so.)
+# past the blob is read.
 
 def test_w4a4_blob_guard_leaves_output_untouched():
     q = require_gpu()
@@ -590,6 +589,58 @@ def test_w4a4_blob_guard_leaves_output_untouched():
     q.gemm_w4a4(ac, as_, at, nv, m, n, k, y=y)
     torch.cuda.synchronize()
     assert not torch.any(y == 7.0)
+
+
+# The decode kernels read the header with their first weight loads and test
+# it before their first store: a blob of another format or shape, at least as
+# large as the expected one (so every read stays inside it), leaves y as it
+# was.  Each kernel path: persistent (at least two row tiles per CU,
+# k <= 4096), k-split (few row tiles), pipelined long k (m <= 16), and the k
+# split over blocks with a workspace (long k, 8 < m <= 32).
+
+@pytest.mark.parametrize("n,k,m", [(16384, 1024, 3), (272, 1024, 5), (272, 8192, 7),
+                                   (272, 8192, 12)])
+def test_decode_blob_guard_leaves_output_untouched(n, k, m):
+    q = require_gpu()
+    w = synth.weights(16, 0, n, k)
+    nv, i4, l2 = _nvfp4_blob(q, w), _int4_blob(q, w), _lut2_blob(q, w)
+    c24, s24 = q.quantize_int4_g128(dev_f32(w), sparse24=True)
+    sp = q.repack_weights(q.QL_INT4_SP24, n, k, c24, s24)
+    w2 = synth.weights(16, 1, 2 * n, k)
+    i4_2n, l2_2n = _int4_blob(q, w2), _lut2_blob(q, w2)        # packed for another n
+    w3 = synth.weights(16, 2, n, 2 * k)
+    i4_2k = _int4_blob(q, w3)                                  # packed for another k
+    xb = dev_bf16(synth.activations_bf16(16, 0, m, k))
+    say("decode blob guard", n, k, m)
+    ws4 = torch.empty(max(16, q.gemm_w4a16_workspace(m, n, k)), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty(max(16, q.gemm_lut2_workspace(m, n, k)), dtype=torch.uint8, device="cuda")
+    cases = [
+        ("w4a16 given an NVFP4 blob", q.gemm_w4a16, nv, None),
+        ("w4a16 given an INT4 blob of 2n rows", q.gemm_w4a16, i4_2n, None),
+        ("w4a16 given an INT4 blob of 2k columns", q.gemm_w4a16, i4_2k, None),
+        ("w4a16 (workspace) given an INT4 blob of 2k columns", q.gemm_w4a16, i4_2k, ws4),
+        ("lut2 given an INT4 blob", q.gemm_lut2, i4, None),
+        ("lut2 given a LUT2 blob of 2n rows", q.gemm_lut2, l2_2n, None),
+        ("lut2 (workspace) given an INT4 blob", q.gemm_lut2, i4, ws2),
+        ("sp24 given an INT4 blob", q.gemm_w4a16_sp24, i4, None),
+    ]
+    for name, fn, blob, ws in cases:
+        assert blob.numel() >= q.repack_weights_bytes(
+            {q.gemm_w4a16: q.QL_INT4_G128, q.gemm_lut2: q.QL_LUT2,
+             q.gemm_w4a16_sp24: q.QL_INT4_SP24}[fn], n, k), name
+        y = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
+        if fn is q.gemm_w4a16_sp24:
+            fn(xb, blob, n, k, y=y)
+        else:
+            fn(xb, blob, n, k, y=y, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.all(y == 7.0), name
+    # and the right blobs do write
+    for fn, blob in ((q.gemm_w4a16, i4), (q.gemm_lut2, l2), (q.gemm_w4a16_sp24, sp)):
+        y = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
+        fn(xb, blob, n, k, y=y)
+        torch.cuda.synchronize()
+        assert not torch.any(y == 7.0)
 
 
 def test_binding_rejects_undersized_buffers():
