@@ -348,19 +348,16 @@ hipError_t launch_sp24_ksplit_w(const uint16_t* x, const uint8_t* blob, const Bl
                                 int M, int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int gpw = (K / 128 + KW - 1) / KW;
   const int rows = M - m0 < 16 * MT ? M - m0 : 16 * MT;
-  // (two m-tiles of two row tiles keep per-group loads: the staged rows would
-  // not fit next to the chunk's weights)
-  if constexpr (W <= 4 && MT * NTB <= 2) {
+  if constexpr (W <= 4) {
     if (gpw <= W) {
-      if constexpr (MT == 2) {
-        return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-      } else {
-        switch (stage_quads(rows, MT)) {
-          case 0: return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-          case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-          case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-          default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-        }
+      switch (stage_quads(rows, MT)) {
+        case 0:
+          if constexpr (MT == 1)
+            return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+          break;
+        case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
       }
     }
   }
