@@ -966,21 +966,23 @@ DecodeSplit decode_split_plan(bool lut, int64_t m, int64_t n, int64_t k) {
   // Measured against the unsplit kernels (graph replay over rotating weight
   // copies, Qwen3-8B-like and Gemma3-like decode shapes): the split pays only
   // where k is long and the batch large enough that every block loading the
-  // whole activation dominates -- W4A16 4096 x 12288 at M = 16 1.04x, M = 32
-  // 1.66x; LUT2 3840 x 15360 at M = 16 1.09x -- and costs 0.6-0.9x at M <= 8
-  // and on K <= 4096 (the second launch adds ~1.7 us).
+  // whole activation dominates -- W4A16 4096 x 12288 at M = 9 / 16 / 32:
+  // 11.9 / 12.4 / 27.7 us unsplit, 10.5 / 11.4 / 16.3 us split; LUT2
+  // 3840 x 15360 at M = 9 / 16: 12.2 / 13.5 us unsplit, 11.2 / 12.0 us split
+  // -- and costs 0.6-0.9x at M <= 8 and on K <= 4096 (the second launch adds
+  // ~1.7 us).  One block per CU (S P = CUs) measured best: walkers sharing a
+  // CU slowed every split plan by 5-30 %.
   if (G <= KW * 4 || m <= 8) return best;
   int64_t best_cost = INT64_MAX;
   for (int gw = 1; gw <= 4; ++gw) {
     if (mt == 2 && lut && gw > 2) break;
     const int64_t S = (G + nw * gw - 1) / (nw * gw);
     if (S < 2) continue;
-    const int bpc = persist_blocks_per_cu(gw, mt, lut);
-    const int64_t P = std::min<int64_t>(T, int64_t(bpc) * cus / S);
+    const int64_t P = std::min<int64_t>(T, cus / S);
     if (P < 1) continue;
     // (row tile, group) units per CU, plus a round trip per pair of tiles
     const int64_t tiles = (T + P - 1) / P;
-    const int64_t cost = tiles * nw * gw * bpc + 32 * ((tiles + 1) / 2);
+    const int64_t cost = tiles * nw * gw + 32 * ((tiles + 1) / 2);
     if (cost < best_cost) {
       best_cost = cost;
       best = DecodeSplit{gw, mt, int(S), int(P)};
