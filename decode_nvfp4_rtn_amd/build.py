@@ -1,6 +1,7 @@
 """Build libqlin.so (hand-written HIP for gfx950) in-tree.
 
-    python -m decode_nvfp4_rtn_amd.build
+    python -m decode_nvfp4_rtn_amd.build              # libqlin.so
+    python -m decode_nvfp4_rtn_amd.build --sanitize   # host ASan/UBSan build
 
 Each translation unit is compiled with hipcc for gfx950 only, then linked
 into ``decode_nvfp4_rtn_amd/libqlin.so``.  Flags:
@@ -51,8 +52,29 @@ def _hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, src + ".o")
+# Host code with AddressSanitizer and UndefinedBehaviorSanitizer (each flag
+# after -Xarch_host: the device code is built exactly as in libqlin.so).  The
+# library expects the sanitizer runtime to be preloaded into the process
+# (LD_PRELOAD of sanitizer_runtime()); tests/test_abi_sanitized.py runs the
+# C-ABI tests on it.
+SANITIZE = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+BUILD_SAN = os.path.join(HERE, "_build_asan")
+LIB_SAN = os.path.join(BUILD_SAN, "libqlin_asan.so")
+
+
+def sanitizer_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime (with UBSan)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def _compile(src, extra, out_dir=BUILD):
+    obj = os.path.join(out_dir, src + ".o")
     cmd = [_hipcc(), *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -76,6 +98,29 @@ def build(verbose=True):
     return LIB
 
 
+def build_sanitized(verbose=True):
+    """The same sources with sanitized host code, linked into
+    _build_asan/libqlin_asan.so (not loaded by the package); returns its path."""
+    os.makedirs(BUILD_SAN, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda kv: _compile(kv[0], [*kv[1], *SANITIZE], BUILD_SAN),
+                           SOURCES.items()))
+    tmp = LIB_SAN + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB_SAN)
+    if verbose:
+        print(f"built {LIB_SAN}")
+    return LIB_SAN
+
+
 if __name__ == "__main__":
-    build()
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized()
+    else:
+        build()
     sys.exit(0)

@@ -10,7 +10,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "qlin.h")
-LIB = os.path.join(ROOT, "decode_nvfp4_rtn_amd", "libqlin.so")
+# QLIN_ABI_LIB: another build of the same library (the sanitized host build
+# in test_abi_sanitized.py)
+LIB = os.environ.get("QLIN_ABI_LIB") or os.path.join(ROOT, "decode_nvfp4_rtn_amd", "libqlin.so")
 
 QL_OK, QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EDTYPE, QL_EWORKSPACE, QL_EHIP, QL_EFORMAT = range(8)
 
