@@ -715,6 +715,24 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
     __builtin_amdgcn_sched_barrier(0);   // keep the tile loads ahead of the seed arithmetic
   }
 
+  // slots past the last group (g0 + i >= G: the last k slice, or K not a
+  // multiple of the groups a block covers) loaded a clamped copy of group
+  // G - 1; their activation fragments are zeroed here, once, so that their
+  // products vanish in every tile with no per-tile masking of the weights
+  // (finite codebook entries and scales times zero)
+  const bf16x8_t zero8 = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    if (g0 + i >= G) {   // wave-uniform
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int mt = 0; mt < MR; ++mt) xf[i][s][mt] = zero8;
+        if constexpr (kXL) xt[i][s] = zero8;
+      }
+    }
+  }
+
   floatx4 xs[GW][MT];
   if constexpr (!kLut) {
 #pragma unroll
@@ -749,11 +767,9 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
       for (int mt = 0; mt < MT; ++mt) t2[0][mt] = t2[1][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
-        const uint32_t keep = g0 + i < G ? 0xFFFFFFFFu : 0u;   // else zero codebook
-        const uint32_t lo = A.book.x & keep, hi = A.book.y & keep;
         bf16x8_t a[4];
-        lut2_operands(A.w[i].x, lo, hi, a[0], a[1]);
-        lut2_operands(A.w[i].y, lo, hi, a[2], a[3]);
+        lut2_operands(A.w[i].x, A.book.x, A.book.y, a[0], a[1]);
+        lut2_operands(A.w[i].y, A.book.x, A.book.y, a[2], a[3]);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -785,8 +801,7 @@ void decode_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __rest
       }
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
-        const bool live = g0 + i < G;
-        const uint32_t s01 = live ? A.s[i].x : 0u, s23 = live ? A.s[i].y : 0u;
+        const uint32_t s01 = A.s[i].x, s23 = A.s[i].y;
         const float sc[4] = {__uint_as_float(s01 << 16), __uint_as_float(s01 & 0xFFFF0000u),
                              __uint_as_float(s23 << 16), __uint_as_float(s23 & 0xFFFF0000u)};
 #pragma unroll
