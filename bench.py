@@ -123,6 +123,50 @@ def draw_weights(cid, li, n, k):
     return out
 
 
+def decode_launches(spec, dev, bf16, f32):
+    """Profiling workload (--decode-launches): the named decode cases in the
+    given order, each as 3 direct launches, each launch after a 512 MiB device
+    fill (twice the Infinity Cache) so the weights come from HBM."""
+    import torch
+    from decode_nvfp4_rtn_amd import qlin, synth, configs
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for case in spec.split(","):
+        parts = case.strip().split("/")
+        kind, name, m = parts[0], parts[1], int(parts[2])
+        use_ws = parts[3:] == ["ws"]
+        cfg = configs.GEMMA3_LUT2 if kind == "lut2" else configs.QWEN3_DECODE
+        li = [L.name for L in cfg.layers].index(name)
+        L = cfg.layers[li]
+        w = f32(synth.weights(cfg.cid, li, L.n, L.k))
+        if kind == "lut2":
+            i, c = qlin.fit_lut2(w)
+            blob = qlin.repack_weights(qlin.QL_LUT2, L.n, L.k, i, c)
+            fn, wsf = qlin.gemm_lut2, qlin.gemm_lut2_workspace
+        elif kind == "sp24":
+            c, sc = qlin.quantize_int4_g128(w, sparse24=True)
+            blob = qlin.repack_weights(qlin.QL_INT4_SP24, L.n, L.k, c, sc)
+            fn, wsf = qlin.gemm_w4a16_sp24, None
+        else:
+            c, sc = qlin.quantize_int4_g128(w)
+            blob = qlin.repack_weights(qlin.QL_INT4_G128, L.n, L.k, c, sc)
+            fn, wsf = qlin.gemm_w4a16, qlin.gemm_w4a16_workspace
+        del w
+        x = bf16(synth.decode_x_bf16(cfg.cid, li, m, L.k))
+        y = torch.empty((m, L.n), dtype=torch.bfloat16, device=dev)
+        kw = {}
+        if use_ws:
+            nb = wsf(m, L.n, L.k) if wsf else 0
+            if nb == 0:
+                raise SystemExit(f"{case}: this shape has no k-split workspace")
+            kw["workspace"] = torch.empty(nb, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for r in range(3):
+            flush.fill_(r)
+            fn(x, blob, L.n, L.k, y=y, **kw)
+            torch.cuda.synchronize()
+        print(f"case {case}: {L.n} x {L.k}, m {m}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +193,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run 3 device copies of 256 MiB (a kernel of known traffic, "
                          "to scale the FETCH_SIZE/WRITE_SIZE counters of a --pmc run)")
+    ap.add_argument("--decode-launches", default=None, metavar="CASES",
+                    help="profiling workload only: comma-separated decode cases "
+                         "format/layer/M[/ws] (format w4a16, sp24 or lut2; layer as in the "
+                         "decode sweep; ws: the workspace entry point), each launched 3 times "
+                         "after a 512 MiB fill that evicts the weights from the Infinity "
+                         "Cache; prints one line per case and no bench line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -172,6 +222,10 @@ def main():
 
     def f32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    if args.decode_launches:
+        decode_launches(args.decode_launches, dev, bf16, f32)
+        return
 
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
