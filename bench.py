@@ -191,8 +191,9 @@ def main():
     ap.add_argument("--no-odp", action="store_true",
                     help="skip the host-to-device weight streaming measurement")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run 3 device copies of 256 MiB (a kernel of known traffic, "
-                         "to scale the FETCH_SIZE/WRITE_SIZE counters of a --pmc run)")
+                    help="first run 3 device copies and 3 elementwise negations of 256 MiB "
+                         "(kernels of known traffic, to scale the FETCH_SIZE/WRITE_SIZE "
+                         "counters of a --pmc run)")
     ap.add_argument("--decode-launches", default=None, metavar="CASES",
                     help="profiling workload only: comma-separated decode cases "
                          "format/layer/M[/ws] (format w4a16, sp24 or lut2; layer as in the "
@@ -228,12 +229,19 @@ def main():
         return
 
     if args.copy_calibration:
+        # kernels of known traffic: three runtime copies of 256 MiB, then three
+        # elementwise negations of 256 MiB of fp32 (a plain vector kernel that
+        # reads 256 MiB and writes 256 MiB with ordinary loads and stores)
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
+        af, bf = a.view(torch.float32), b.view(torch.float32)
+        af.zero_()
+        for _ in range(3):
+            torch.neg(af, out=bf)
         torch.cuda.synchronize()
-        del a, b
+        del a, b, af, bf
 
     def prefill_set(cfg, m_max, ms):
         """Packed weights, full-size activations and output buffers of a
