@@ -256,15 +256,20 @@ __global__ __launch_bounds__(KW * 64) void sp24_ksplit_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) tot[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // XQ >= 0 (the wave's groups fit one chunk): the activation rows of all
-  // its groups are loaded first and staged (rows_stage) once the chunk's
-  // weight loads are in flight; XQ < 0 loads each group's operands directly
+  // XQ >= 0: the activation rows of a chunk's groups are loaded first and
+  // staged (rows_stage) once the chunk's weight loads are in flight -- per
+  // chunk with one m-tile; with two (whose registers hold one chunk's rows
+  // only next to the rest) the launcher takes this form only when the
+  // wave's groups fit one chunk, loaded ahead of the loop.  XQ < 0 loads
+  // each group's operands directly.
   __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KW : 1][4096];
   bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
-  if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
+  if constexpr (XQ >= 0 && MT == 2) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
 
   uint32_t hdr = 0;   // header words (lane l: word l % 8)
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
+    if constexpr (XQ >= 0 && MT == 1)
+      rows_load<WMAX, MT, XQ>(x, M, m0, K, g0 + c0, gpw - c0, G, lane, xpre);
     SpGroup w[WMAX][NTB];
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
@@ -348,17 +353,18 @@ hipError_t launch_sp24_ksplit_w(const uint16_t* x, const uint8_t* blob, const Bl
                                 int M, int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int gpw = (K / 128 + KW - 1) / KW;
   const int rows = M - m0 < 16 * MT ? M - m0 : 16 * MT;
-  if constexpr (W <= 4) {
-    if (gpw <= W) {
-      switch (stage_quads(rows, MT)) {
-        case 0:
-          if constexpr (MT == 1)
-            return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-          break;
-        case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-        case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-        default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
-      }
+  // one m-tile: rows staged per chunk (chunks of up to six groups); two
+  // m-tiles: only when the wave's groups fit one chunk of up to four
+  if constexpr (MT == 1 ? W <= 6 : W <= 4) {
+    if (MT == 2 && gpw > W) return launch_sp24_ksplit_xq<MT, NTB, W, -1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+    switch (stage_quads(rows, MT)) {
+      case 0:   // one token: a lane per group for up to four groups, else one row quad
+        if constexpr (MT == 1 && W <= 4)
+          return launch_sp24_ksplit_xq<MT, NTB, W, 0>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+        return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      case 1: return launch_sp24_ksplit_xq<MT, NTB, W, 1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      case 2: return launch_sp24_ksplit_xq<MT, NTB, W, 2>(x, blob, L, M, m0, N, K, y, y_dtype, s);
+      default: return launch_sp24_ksplit_xq<MT, NTB, W, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
     }
   }
   return launch_sp24_ksplit_xq<MT, NTB, W, -1>(x, blob, L, M, m0, N, K, y, y_dtype, s);

@@ -95,7 +95,8 @@ def test_sp24_qwen3_decode_all_batches(li):
         _check(host_f64(y16), ref, True)
 
 
-@pytest.mark.parametrize("n,k", [(16 * 1031, 3840), (16 * 1537, 2048), (272, 8320), (6160, 1152)])
+@pytest.mark.parametrize("n,k", [(16 * 1031, 3840), (16 * 1537, 2048), (272, 8320), (272, 12288),
+                                 (6160, 1152)])
 def test_sp24_ragged_shapes_both_kernels(n, k):
     q = require_gpu()
     w = synth.weights(11, 3, n, k)
