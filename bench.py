@@ -145,7 +145,7 @@ def decode_launches(spec, dev, bf16, f32):
         elif kind == "sp24":
             c, sc = qlin.quantize_int4_g128(w, sparse24=True)
             blob = qlin.repack_weights(qlin.QL_INT4_SP24, L.n, L.k, c, sc)
-            fn, wsf = qlin.gemm_w4a16_sp24, None
+            fn, wsf = qlin.gemm_w4a16_sp24, qlin.gemm_w4a16_sp24_workspace
         else:
             c, sc = qlin.quantize_int4_g128(w)
             blob = qlin.repack_weights(qlin.QL_INT4_G128, L.n, L.k, c, sc)
@@ -155,7 +155,7 @@ def decode_launches(spec, dev, bf16, f32):
         y = torch.empty((m, L.n), dtype=torch.bfloat16, device=dev)
         kw = {}
         if use_ws:
-            nb = wsf(m, L.n, L.k) if wsf else 0
+            nb = wsf(m, L.n, L.k)
             if nb == 0:
                 raise SystemExit(f"{case}: this shape has no k-split workspace")
             kw["workspace"] = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -347,7 +347,8 @@ def main():
         x32 = {m: bf16(synth.decode_x_bf16(dec.cid, li, m, L.k)) for m in dec.ms}
         D.append(dict(L=L, blob=blob, blob24=blob24, x=x32,
                       y={m: torch.empty((m, L.n), dtype=torch.bfloat16, device=dev) for m in dec.ms},
-                      ws=decode_ws(qlin.gemm_w4a16_workspace, dec.ms, L)))
+                      ws=decode_ws(qlin.gemm_w4a16_workspace, dec.ms, L),
+                      ws24=decode_ws(qlin.gemm_w4a16_sp24_workspace, dec.ms, L)))
     U = []   # LUT2 decode layers
     for li, L in enumerate(lut.layers):
         i, c = qlin.fit_lut2(f32(draw_weights(lut.cid, li, L.n, L.k)))
@@ -479,7 +480,7 @@ def main():
             if m == (lut.ms if kind == "lut2" else dec.ms)[0]:
                 copies = [src.clone() for _ in range(int(np.ceil(600e6 / src.numel())))]
             x, y = rec["x"][m], rec["y"][m]
-            kw = {} if kind == "w4a16_sp24" else {"workspace": rec["ws"][m]}
+            kw = {"workspace": rec["ws24" if kind == "w4a16_sp24" else "ws"][m]}
             for b in copies[:3]:
                 fn(x, b, L.n, L.k, y=y, **kw)
             torch.cuda.synchronize()

@@ -212,16 +212,19 @@ int gemm_lut2(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, in
                                         as_stream(stream)));
 }
 
-static size_t decode_ws(bool lut, int64_t m, int64_t n, int64_t k) {
+// fmt: 1 INT4, 2 LUT2, 3 INT4 2:4 sparse
+static size_t decode_ws(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || n % 16 != 0 || k % 128 != 0) return 0;
   if (m > (int64_t(1) << 31) / 2 || n > (int64_t(1) << 24) || k > (int64_t(1) << 20)) return 0;
-  return decode_split_bytes(decode_split_plan(lut, m, n, k), m, n);
+  const DecodeSplit p = fmt == 3 ? sp24_split_plan(m, n, k) : decode_split_plan(fmt == 2, m, n, k);
+  return decode_split_bytes(p, m, n);
 }
 
-size_t gemm_w4a16_workspace(int64_t m, int64_t n, int64_t k) { return decode_ws(false, m, n, k); }
-size_t gemm_lut2_workspace(int64_t m, int64_t n, int64_t k) { return decode_ws(true, m, n, k); }
+size_t gemm_w4a16_workspace(int64_t m, int64_t n, int64_t k) { return decode_ws(1, m, n, k); }
+size_t gemm_lut2_workspace(int64_t m, int64_t n, int64_t k) { return decode_ws(2, m, n, k); }
+size_t gemm_w4a16_sp24_workspace(int64_t m, int64_t n, int64_t k) { return decode_ws(3, m, n, k); }
 
-static int decode_ws_call(bool lut, const void* x_bf16, const void* w_packed, int64_t m, int64_t n,
+static int decode_ws_call(int fmt, const void* x_bf16, const void* w_packed, int64_t m, int64_t n,
                           int64_t k, void* y, int y_dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
   int st = check_gemm(w_packed, y, m, n, k, y_dtype);
@@ -230,23 +233,31 @@ static int decode_ws_call(bool lut, const void* x_bf16, const void* w_packed, in
   if (!aligned16(x_bf16)) return QL_EALIGN;
   if (workspace) {
     if (!aligned16(workspace)) return QL_EALIGN;
-    if (workspace_bytes < decode_ws(lut, m, n, k)) return QL_EWORKSPACE;
+    if (workspace_bytes < decode_ws(fmt, m, n, k)) return QL_EWORKSPACE;
   }
-  return launch_status(lut ? launch_gemm_lut2(x_bf16, w_packed, m, n, k, y, y_dtype, workspace,
-                                              workspace_bytes, as_stream(stream))
-                           : launch_gemm_w4a16(x_bf16, w_packed, m, n, k, y, y_dtype, workspace,
-                                               workspace_bytes, as_stream(stream)));
+  hipStream_t s = as_stream(stream);
+  switch (fmt) {
+    case 2:
+      return launch_status(launch_gemm_lut2(x_bf16, w_packed, m, n, k, y, y_dtype, workspace,
+                                            workspace_bytes, s));
+    case 3:
+      return launch_status(launch_gemm_w4a16_sp24(x_bf16, w_packed, m, n, k, y, y_dtype,
+                                                  workspace, workspace_bytes, s));
+    default:
+      return launch_status(launch_gemm_w4a16(x_bf16, w_packed, m, n, k, y, y_dtype, workspace,
+                                             workspace_bytes, s));
+  }
 }
 
 int gemm_w4a16_ws(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, int64_t k,
                   void* y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_ws_call(false, x_bf16, w_packed, m, n, k, y, y_dtype, workspace, workspace_bytes,
+  return decode_ws_call(1, x_bf16, w_packed, m, n, k, y, y_dtype, workspace, workspace_bytes,
                         stream);
 }
 
 int gemm_lut2_ws(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, int64_t k,
                  void* y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_ws_call(true, x_bf16, w_packed, m, n, k, y, y_dtype, workspace, workspace_bytes,
+  return decode_ws_call(2, x_bf16, w_packed, m, n, k, y, y_dtype, workspace, workspace_bytes,
                         stream);
 }
 
@@ -256,8 +267,15 @@ int gemm_w4a16_sp24(const void* x_bf16, const void* w_packed, int64_t m, int64_t
   if (st >= 0) return st;
   if (!x_bf16) return QL_EINVAL;
   if (!aligned16(x_bf16)) return QL_EALIGN;
-  return launch_status(launch_gemm_w4a16_sp24(x_bf16, w_packed, m, n, k, y, y_dtype,
+  return launch_status(launch_gemm_w4a16_sp24(x_bf16, w_packed, m, n, k, y, y_dtype, nullptr, 0,
                                               as_stream(stream)));
+}
+
+int gemm_w4a16_sp24_ws(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, int64_t k,
+                       void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return decode_ws_call(3, x_bf16, w_packed, m, n, k, y, y_dtype, workspace, workspace_bytes,
+                        stream);
 }
 
 }  // extern "C"

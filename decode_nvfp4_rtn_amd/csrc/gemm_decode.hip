@@ -1063,15 +1063,7 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
       }
     }
     if (e != hipSuccess) return e;
-    const int64_t n4 = m * n / 4;
-    const int rb = int((n4 + 255) / 256);
-    if (y_dtype == 1)
-      decode_reduce_kernel<true><<<rb, 256, 0, s>>>(part, sp.S, n4, y, blob, kLut ? 2 : 1, int(n),
-                                                    int(k));
-    else
-      decode_reduce_kernel<false><<<rb, 256, 0, s>>>(part, sp.S, n4, y, blob, kLut ? 2 : 1, int(n),
-                                                     int(k));
-    return hipGetLastError();
+    return launch_decode_reduce(part, sp.S, m, n, y, y_dtype, blob, kLut ? 2 : 1, k, s);
   }
   // one pass over the batch (M <= 32), K <= 4096 and at least two row tiles
   // per CU: persistent kernel
@@ -1139,6 +1131,18 @@ hipError_t launch_decode_all(const void* x, const void* w_packed, int64_t m, int
 }
 
 }  // namespace
+
+hipError_t launch_decode_reduce(const float* part, int S, int64_t m, int64_t n, void* y,
+                                int y_dtype, const uint8_t* blob, int fmt, int64_t k,
+                                hipStream_t s) {
+  const int64_t n4 = m * n / 4;
+  const int rb = int((n4 + 255) / 256);
+  if (y_dtype == 1)
+    decode_reduce_kernel<true><<<rb, 256, 0, s>>>(part, S, n4, y, blob, fmt, int(n), int(k));
+  else
+    decode_reduce_kernel<false><<<rb, 256, 0, s>>>(part, S, n4, y, blob, fmt, int(n), int(k));
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int64_t n, int64_t k,
                              void* y, int y_dtype, void* ws, size_t ws_bytes, hipStream_t s) {

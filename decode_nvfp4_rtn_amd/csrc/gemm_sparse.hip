@@ -23,6 +23,9 @@
 // so each chain starts with one more sparse MFMA of an all -136 operand with
 // the same positions (sum over the kept k of -136 x).
 #include "qlin_internal.hpp"
+#include <algorithm>
+#include <climits>
+
 #include "decode_ops.hpp"
 
 namespace qlin {
@@ -109,27 +112,31 @@ __device__ __forceinline__ void store_one(void* y, int64_t idx, float v) {
     static_cast<float*>(y)[idx] = v;
 }
 
-// Persistent kernel for MT m-tiles (M <= 16 MT), K <= 128 * KW * GW and at
-// least two row tiles per block, organised as the dense persistent kernel:
-// wave w owns groups [GW w, GW w + GW) of every row tile and keeps their
-// activation fragments in registers; blocks walk the row tiles with the next
-// tile's weights in flight; 4 MT waves add the eight partial sums of a tile
-// (one component and m-tile each).  The dequantized operand of a group is
-// shared by the m-tiles.
+// Persistent kernel for MT m-tiles (M <= 16 MT), K <= 128 * KW * GW per k
+// slice and at least two row tiles per block, organised as the dense
+// persistent kernel: wave w owns groups [GW w, GW w + GW) of its slice in
+// every row tile and keeps their activation fragments in registers; blocks
+// walk the row tiles with the next tile's weights in flight; 4 MT waves add
+// the eight partial sums of a tile (one component and m-tile each).  The
+// dequantized operand of a group is shared by the m-tiles.  With S > 1 k
+// slices (the workspace entry point), block b serves slice b % S, walks
+// tiles b / S, + gridDim.x / S, ... and stores the slice's fp32 partial sums
+// to part[slice][m][n]; a second launch adds the slices.
 constexpr int sp_blocks_per_cu(int gw, int mt) { return gw == 2 && mt == 1 ? 2 : 1; }
 
 template <int GW, int MT, int XQ, bool kBF16Out>
 __global__ __launch_bounds__(KW * 64, KW / 4 * sp_blocks_per_cu(GW, MT))
 void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ blob,
                          int64_t codes_off, int64_t aux_off, int M, int N, int K,
-                         void* __restrict__ y) {
+                         void* __restrict__ y, int S, float* __restrict__ part) {
   const uint32_t hdr = header_word(blob);   // tested before the first store
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int G = K / 128;
-  const int g0 = wave * GW;
+  const int sl = blockIdx.x % S;          // k slice: groups [KW GW sl, KW GW (sl + 1))
+  const int g0 = (sl * KW + wave) * GW;
   const int T = N / 16;
-  const int stride = gridDim.x;
+  const int stride = gridDim.x / S;       // tile walkers per slice
   const uint32_t m136 = vconst(0xC308C308u);
   const bf16x8_t neg136 = as_bf16x8(u32x4{m136, m136, m136, m136});
   const uint32_t nib_mask = vconst(0x000F000Fu), bf16_128 = vconst(0x43004300u);
@@ -150,7 +157,7 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KW : 1][4096];
   bf16x16_t xh[MT][GW][2];
   Tile A, B;
-  int t = blockIdx.x;
+  int t = blockIdx.x / S;
   if constexpr (XQ >= 0) {
     bf16x8_t f[GW][4][MT];
     rows_load<GW, MT, XQ>(x, M, 0, K, g0, GW, G, lane, f);
@@ -204,11 +211,16 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
 #pragma unroll
         for (int w = 0; w < h; ++w) v[w] += v[w + h];
       const int m = mt * 16 + (lane & 15), n = t * 16 + 4 * (lane >> 4) + r;
-      if (m < M) store_one<kBF16Out>(y, int64_t(m) * N + n, v[0]);
+      if (m < M) {
+        if (S > 1)
+          part[(int64_t(sl) * M + m) * N + n] = v[0];   // this slice's partial sum
+        else
+          store_one<kBF16Out>(y, int64_t(m) * N + n, v[0]);
+      }
     }
   };
 
-  // the launch guarantees gridDim.x <= T; the second tile of an iteration is
+  // the launch guarantees gridDim.x / S <= T; the second tile of an iteration is
   // computed from clamped loads but not stored when it does not exist (no
   // branch around the waits, which would also wait for the prefetch)
   for (; t < T; t += 2 * stride) {
@@ -382,54 +394,106 @@ hipError_t launch_sp24_ksplit(const uint16_t* x, const uint8_t* blob, const Blob
   }
 }
 
+// grid: S k slices x tile walkers (at most T per slice); part: the fp32
+// partial sums when S > 1
 template <int GW, int MT, int XQ>
 hipError_t launch_sp24_persist_xq(const uint16_t* x, const uint8_t* blob, const BlobLayout& L,
-                                  int M, int N, int K, void* y, int y_dtype, int cus,
-                                  hipStream_t s) {
-  const int T = N / 16, per_cu = sp_blocks_per_cu(GW, MT);
-  // every block owns at least two tiles, and the grid never exceeds T
-  const int grid = T >= 2 * per_cu * cus ? per_cu * cus : cus;
+                                  int M, int N, int K, void* y, int y_dtype, int grid, int S,
+                                  float* part, hipStream_t s) {
   if (y_dtype == 1)
-    sp24_persist_kernel<GW, MT, XQ, true><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off,
-                                                                   L.aux_off, M, N, K, y);
+    sp24_persist_kernel<GW, MT, XQ, true><<<grid, KW * 64, 0, s>>>(
+        x, blob, L.codes_off, L.aux_off, M, N, K, y, S, part);
   else
-    sp24_persist_kernel<GW, MT, XQ, false><<<grid, KW * 64, 0, s>>>(x, blob, L.codes_off,
-                                                                    L.aux_off, M, N, K, y);
+    sp24_persist_kernel<GW, MT, XQ, false><<<grid, KW * 64, 0, s>>>(
+        x, blob, L.codes_off, L.aux_off, M, N, K, y, S, part);
   return hipGetLastError();
 }
 
 template <int GW, int MT>
 hipError_t launch_sp24_persist(const uint16_t* x, const uint8_t* blob, const BlobLayout& L, int M,
-                               int N, int K, void* y, int y_dtype, int cus, hipStream_t s) {
+                               int N, int K, void* y, int y_dtype, int grid, int S, float* part,
+                               hipStream_t s) {
   if constexpr (MT == 2)
-    return launch_sp24_persist_xq<GW, MT, 4>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+    return launch_sp24_persist_xq<GW, MT, 4>(x, blob, L, M, N, K, y, y_dtype, grid, S, part, s);
   switch (stage_quads(M, MT)) {
     case 0:
       if constexpr (MT == 1)
-        return launch_sp24_persist_xq<GW, MT, 0>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+        return launch_sp24_persist_xq<GW, MT, 0>(x, blob, L, M, N, K, y, y_dtype, grid, S, part, s);
       break;
-    case 1: return launch_sp24_persist_xq<GW, MT, 1>(x, blob, L, M, N, K, y, y_dtype, cus, s);
-    case 2: return launch_sp24_persist_xq<GW, MT, 2>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+    case 1: return launch_sp24_persist_xq<GW, MT, 1>(x, blob, L, M, N, K, y, y_dtype, grid, S, part, s);
+    case 2: return launch_sp24_persist_xq<GW, MT, 2>(x, blob, L, M, N, K, y, y_dtype, grid, S, part, s);
     default: break;
   }
-  return launch_sp24_persist_xq<GW, MT, 4>(x, blob, L, M, N, K, y, y_dtype, cus, s);
+  return launch_sp24_persist_xq<GW, MT, 4>(x, blob, L, M, N, K, y, y_dtype, grid, S, part, s);
 }
 
 }  // namespace
 
+// Plan of the k-sliced persistent kernel for the workspace entry point: GW
+// groups per wave (2 or 4), S slices of KW GW groups, P tile walkers per
+// slice, one block per CU (S P = CUs), as the dense plan.  Long k and
+// 8 < m <= 32 only, where every block loading the whole activation dominates.
+DecodeSplit sp24_split_plan(int64_t m, int64_t n, int64_t k) {
+  DecodeSplit best{0, 0, 0, 0};
+  const int cus = device_cu_count();
+  if (m < 1 || m > 32 || cus <= 0 || n % 16 != 0 || k % 128 != 0) return best;
+  const int64_t T = n / 16, G = k / 128;
+  if (G <= KW * 4 || m <= 8) return best;
+  int64_t best_cost = INT64_MAX;
+  for (int gw = 2; gw <= 4; gw += 2) {
+    const int64_t S = (G + KW * gw - 1) / (KW * gw);
+    if (S < 2) continue;
+    const int64_t P = std::min<int64_t>(T, cus / S);
+    if (P < 1) continue;
+    // (row tile, group) units per CU, plus a round trip per pair of tiles
+    const int64_t tiles = (T + P - 1) / P;
+    const int64_t cost = tiles * KW * gw + 32 * ((tiles + 1) / 2);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = DecodeSplit{gw, m > 16 ? 2 : 1, int(S), int(P)};
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_w4a16_sp24(const void* x, const void* w_packed, int64_t m, int64_t n,
-                                  int64_t k, void* y, int y_dtype, hipStream_t s) {
+                                  int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                                  hipStream_t s) {
   const BlobLayout L = blob_layout(3, n, k);
   const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const int M = int(m), N = int(n), K = int(k), G = int(k / 128), T = int(n / 16);
   const int cus = device_cu_count();
+  // k split over blocks with the caller's workspace: the slices' fp32
+  // partial sums, added by a second launch
+  const DecodeSplit sp = sp24_split_plan(m, n, k);
+  if (sp.S >= 2 && ws != nullptr && ws_bytes >= decode_split_bytes(sp, m, n)) {
+    float* part = static_cast<float*>(ws);
+    const int grid = sp.S * sp.P;
+    hipError_t e;
+    if (sp.mt == 1)
+      e = sp.gw == 2 ? launch_sp24_persist<2, 1>(xp, blob, L, M, N, K, y, y_dtype, grid, sp.S, part, s)
+                     : launch_sp24_persist<4, 1>(xp, blob, L, M, N, K, y, y_dtype, grid, sp.S, part, s);
+    else
+      e = sp.gw == 2 ? launch_sp24_persist<2, 2>(xp, blob, L, M, N, K, y, y_dtype, grid, sp.S, part, s)
+                     : launch_sp24_persist<4, 2>(xp, blob, L, M, N, K, y, y_dtype, grid, sp.S, part, s);
+    if (e != hipSuccess) return e;
+    return launch_decode_reduce(part, sp.S, m, n, y, y_dtype, blob, 3, k, s);
+  }
   if (m <= 32 && G <= KW * 4 && cus > 0 && T >= 2 * cus) {
+    // every block owns at least two tiles, and the grid never exceeds T
+    auto grid_of = [&](int per_cu) { return T >= 2 * per_cu * cus ? per_cu * cus : cus; };
     if (m <= 16)
-      return G <= KW * 2 ? launch_sp24_persist<2, 1>(xp, blob, L, M, N, K, y, y_dtype, cus, s)
-                         : launch_sp24_persist<4, 1>(xp, blob, L, M, N, K, y, y_dtype, cus, s);
-    return G <= KW * 2 ? launch_sp24_persist<2, 2>(xp, blob, L, M, N, K, y, y_dtype, cus, s)
-                       : launch_sp24_persist<4, 2>(xp, blob, L, M, N, K, y, y_dtype, cus, s);
+      return G <= KW * 2
+                 ? launch_sp24_persist<2, 1>(xp, blob, L, M, N, K, y, y_dtype,
+                                             grid_of(sp_blocks_per_cu(2, 1)), 1, nullptr, s)
+                 : launch_sp24_persist<4, 1>(xp, blob, L, M, N, K, y, y_dtype,
+                                             grid_of(sp_blocks_per_cu(4, 1)), 1, nullptr, s);
+    return G <= KW * 2
+               ? launch_sp24_persist<2, 2>(xp, blob, L, M, N, K, y, y_dtype,
+                                           grid_of(sp_blocks_per_cu(2, 2)), 1, nullptr, s)
+               : launch_sp24_persist<4, 2>(xp, blob, L, M, N, K, y, y_dtype,
+                                           grid_of(sp_blocks_per_cu(4, 2)), 1, nullptr, s);
   }
   const bool wide = T >= 384;   // two row tiles per block still give >= 192 blocks
   for (int64_t m0 = 0; m0 < m; m0 += 32) {

@@ -216,7 +216,16 @@ hipError_t launch_gemm_w4a16(const void* x, const void* w_packed, int64_t m, int
                              int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
                              hipStream_t s);
 hipError_t launch_gemm_w4a16_sp24(const void* x, const void* w_packed, int64_t m, int64_t n,
-                                  int64_t k, void* y, int y_dtype, hipStream_t s);
+                                  int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
+                                  hipStream_t s);
+// 2:4 sparse decode: the k-sliced plan of its workspace entry point (S < 2:
+// no split for this shape).
+DecodeSplit sp24_split_plan(int64_t m, int64_t n, int64_t k);
+// Sum of S slices of fp32 partial sums part[S][m][n] into y (format `fmt`'s
+// blob header tested before the store), in slice order.
+hipError_t launch_decode_reduce(const float* part, int S, int64_t m, int64_t n, void* y,
+                                int y_dtype, const uint8_t* blob, int fmt, int64_t k,
+                                hipStream_t s);
 hipError_t launch_gemm_lut2(const void* x, const void* w_packed, int64_t m, int64_t n,
                             int64_t k, void* y, int y_dtype, void* ws, size_t ws_bytes,
                             hipStream_t s);

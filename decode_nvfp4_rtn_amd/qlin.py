@@ -51,6 +51,8 @@ _SIGS = {
     "gemm_w4a16_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
     "gemm_lut2_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
     "gemm_w4a16_sp24": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
+    "gemm_w4a16_sp24_workspace": (_sz, [_i64, _i64, _i64]),
+    "gemm_w4a16_sp24_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -332,6 +334,10 @@ def gemm_lut2_workspace(m, n, k):
     return _lib.gemm_lut2_workspace(m, n, k)
 
 
+def gemm_w4a16_sp24_workspace(m, n, k):
+    return _lib.gemm_w4a16_sp24_workspace(m, n, k)
+
+
 def _decode(name, fmt, x, w_packed, n, k, y, out_dtype, stream, workspace):
     m = x.shape[0] if x.dim() == 2 else -1
     _rows(x, "x", torch.bfloat16, m, k)
@@ -364,15 +370,13 @@ def gemm_lut2(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None, 
     return _decode("gemm_lut2", QL_LUT2, x, w_packed, n, k, y, out_dtype, stream, workspace)
 
 
-def gemm_w4a16_sp24(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None):
-    """2:4 sparse W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times 2:4 INT4 weights^T."""
-    m = x.shape[0] if x.dim() == 2 else -1
-    _rows(x, "x", torch.bfloat16, m, k)
-    _blob(w_packed, QL_INT4_SP24, n, k)
-    y, dt = _out(y, m, n, out_dtype, x.device)
-    _check("gemm_w4a16_sp24", _lib.gemm_w4a16_sp24(_ptr(x), _ptr(w_packed), m, n, k, _ptr(y), dt,
-                                                   _stream(stream)))
-    return y
+def gemm_w4a16_sp24(x, w_packed, n, k, y=None, out_dtype=torch.bfloat16, stream=None,
+                    workspace=None):
+    """2:4 sparse W4A16 decode GEMM: Y [m, n] = X bf16 [m, k] times 2:4 INT4 weights^T.
+
+    workspace: as gemm_w4a16 (gemm_w4a16_sp24_workspace / gemm_w4a16_sp24_ws)."""
+    return _decode("gemm_w4a16_sp24", QL_INT4_SP24, x, w_packed, n, k, y, out_dtype, stream,
+                   workspace)
 
 
 def raw():

@@ -340,6 +340,25 @@ int gemm_lut2_ws(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
 int gemm_w4a16_sp24(const void *x_bf16, const void *w_packed, int64_t m, int64_t n,
                     int64_t k, void *y, int y_dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * gemm_w4a16_sp24 with a caller-provided workspace for a k split over
+ * blocks, as gemm_w4a16_ws: each block takes one k slice of several 16-row
+ * weight tiles, and a second launch adds the slices' fp32 partial sums in
+ * slice order (deterministic; results differ from gemm_w4a16_sp24's in fp32
+ * rounding only).  Same arithmetic definition and arguments as
+ * gemm_w4a16_sp24, plus the workspace (at least
+ * gemm_w4a16_sp24_workspace(m, n, k) bytes, 16-byte aligned, not read before
+ * it is written; NULL makes the call gemm_w4a16_sp24; calls sharing a
+ * workspace must be ordered).  gemm_w4a16_sp24_workspace returns 0 when no
+ * split applies (it applies to 8 < m <= 32 with k > 4096) and depends on the
+ * current device's compute-unit count.  Errors: as gemm_w4a16_sp24, and
+ * QL_EWORKSPACE when the workspace is non-NULL and too small.
+ * ---------------------------------------------------------------------- */
+size_t gemm_w4a16_sp24_workspace(int64_t m, int64_t n, int64_t k);
+int gemm_w4a16_sp24_ws(const void *x_bf16, const void *w_packed, int64_t m,
+                       int64_t n, int64_t k, void *y, int y_dtype, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,8 @@ def lib():
         "gemm_lut2_workspace": (sz, [i64, i64, i64]),
         "gemm_w4a16_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
         "gemm_lut2_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
+        "gemm_w4a16_sp24_workspace": (sz, [i64, i64, i64]),
+        "gemm_w4a16_sp24_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(L, name)
@@ -149,7 +151,7 @@ def test_decode_gemm_validation(lib, fn):
     assert g(A, B, 0, 16, 128, C, 1, None) == QL_OK
 
 
-@pytest.mark.parametrize("fn", ["gemm_w4a16_ws", "gemm_lut2_ws"])
+@pytest.mark.parametrize("fn", ["gemm_w4a16_ws", "gemm_lut2_ws", "gemm_w4a16_sp24_ws"])
 def test_decode_ws_validation(lib, fn):
     g = getattr(lib, fn)
     assert g(A, B, 1, 20, 128, C, 1, None, 0, None) == QL_ESHAPE
@@ -159,6 +161,7 @@ def test_decode_ws_validation(lib, fn):
     assert g(A, B, 0, 16, 128, C, 1, None, 0, None) == QL_OK
     assert lib.gemm_w4a16_workspace(0, 4096, 12288) == 0
     assert lib.gemm_lut2_workspace(16, 20, 15360) == 0
+    assert lib.gemm_w4a16_sp24_workspace(16, 4096, 12000) == 0
 
 
 def test_w4a4_validation(lib):

@@ -408,14 +408,19 @@ def test_decode_split_workspace_sizes():
     assert q.gemm_lut2_workspace(1, 3840, 15360) == 0
     assert q.gemm_w4a16_workspace(8, 4096, 12288) == 0
     assert q.gemm_w4a16_workspace(33, 4096, 12288) == 0
+    assert q.gemm_w4a16_sp24_workspace(16, 4096, 4096) == 0
+    assert q.gemm_w4a16_sp24_workspace(8, 4096, 12288) == 0
+    assert q.gemm_w4a16_sp24_workspace(33, 4096, 12288) == 0
     # long k with 8 < m <= 32: S slices x m x n fp32 partial sums
-    for ws_fn in (q.gemm_w4a16_workspace, q.gemm_lut2_workspace):
+    for ws_fn in (q.gemm_w4a16_workspace, q.gemm_lut2_workspace, q.gemm_w4a16_sp24_workspace):
         for m, n, k in ((16, 4096, 12288), (9, 3840, 15360), (32, 272, 8320)):
             nb = ws_fn(m, n, k)
             assert nb > 0 and nb % (4 * m * n) == 0 and 2 <= nb // (4 * m * n) <= k // 128
     # too small a workspace is refused before any launch
     lib = q.raw()
     st = lib.gemm_w4a16_ws(1 << 16, 1 << 17, 16, 4096, 12288, 1 << 18, 1, 1 << 19, 16, None)
+    assert st == q.QL_EWORKSPACE
+    st = lib.gemm_w4a16_sp24_ws(1 << 16, 1 << 17, 16, 4096, 12288, 1 << 18, 1, 1 << 19, 16, None)
     assert st == q.QL_EWORKSPACE
 
 
@@ -614,6 +619,8 @@ def test_decode_blob_guard_leaves_output_untouched(n, k, m):
     say("decode blob guard", n, k, m)
     ws4 = torch.empty(max(16, q.gemm_w4a16_workspace(m, n, k)), dtype=torch.uint8, device="cuda")
     ws2 = torch.empty(max(16, q.gemm_lut2_workspace(m, n, k)), dtype=torch.uint8, device="cuda")
+    ws3 = torch.empty(max(16, q.gemm_w4a16_sp24_workspace(m, n, k)), dtype=torch.uint8,
+                      device="cuda")
     cases = [
         ("w4a16 given an NVFP4 blob", q.gemm_w4a16, nv, None),
         ("w4a16 given an INT4 blob of 2n rows", q.gemm_w4a16, i4_2n, None),
@@ -623,16 +630,14 @@ def test_decode_blob_guard_leaves_output_untouched(n, k, m):
         ("lut2 given a LUT2 blob of 2n rows", q.gemm_lut2, l2_2n, None),
         ("lut2 (workspace) given an INT4 blob", q.gemm_lut2, i4, ws2),
         ("sp24 given an INT4 blob", q.gemm_w4a16_sp24, i4, None),
+        ("sp24 (workspace) given an INT4 blob", q.gemm_w4a16_sp24, i4, ws3),
     ]
     for name, fn, blob, ws in cases:
         assert blob.numel() >= q.repack_weights_bytes(
             {q.gemm_w4a16: q.QL_INT4_G128, q.gemm_lut2: q.QL_LUT2,
              q.gemm_w4a16_sp24: q.QL_INT4_SP24}[fn], n, k), name
         y = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
-        if fn is q.gemm_w4a16_sp24:
-            fn(xb, blob, n, k, y=y)
-        else:
-            fn(xb, blob, n, k, y=y, workspace=ws)
+        fn(xb, blob, n, k, y=y, workspace=ws)
         torch.cuda.synchronize()
         assert torch.all(y == 7.0), name
     # and the right blobs do write

@@ -111,6 +111,37 @@ def test_sp24_ragged_shapes_both_kernels(n, k):
         _check(host_f64(y)[:, cols], gemm.w4a16_sp24(xb, rc, rs), False)
 
 
+# The workspace entry point splits k over blocks (S slices of 8 GW groups, P
+# tile walkers per slice): a last slice with fewer groups than the others, a
+# last slice of one group, tile counts that leave walkers a tile short, one
+# and two m-tiles, and every Qwen3-8B-like layer with long k.
+
+@pytest.mark.parametrize("n,k", [(4096, 12288), (272, 8320), (16 * 257, 9088), (6160, 4224),
+                                 (16 * 1031, 8192), (12288, 4608)])
+def test_sp24_split_ragged(n, k):
+    q = require_gpu()
+    w = synth.weights(17, k, n, k)
+    say("sp24 split", n, k)
+    blob, _, _ = _sp24_blob(q, w)
+    rc, rs = orows.sp24_quantize(w)
+    del w
+    ms = (9, 13, 16, 17, 25, 32)
+    xs = [synth.activations_bf16(17, m, m, k) for m in ms]
+    refs = np.split(gemm.w4a16_sp24(np.concatenate(xs), rc, rs), np.cumsum(ms)[:-1])
+    for m, xb, ref in zip(ms, xs, refs):
+        nb = q.gemm_w4a16_sp24_workspace(m, n, k)
+        assert nb > 0, (m, n, k)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        x = dev_bf16(xb)
+        y32 = q.gemm_w4a16_sp24(x, blob, n, k, out_dtype=torch.float32, workspace=ws)
+        y16 = q.gemm_w4a16_sp24(x, blob, n, k, out_dtype=torch.bfloat16, workspace=ws)
+        y16b = q.gemm_w4a16_sp24(x, blob, n, k, out_dtype=torch.bfloat16, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y16, y16b)
+        _check(host_f64(y32), ref, False)
+        _check(host_f64(y16), ref, True)
+
+
 def test_sp24_repack_prunes_dense_codes_by_magnitude():
     q = require_gpu()
     n, k = 64, 1024
