@@ -188,6 +188,8 @@ def main():
                     help="skip the 27B-class prefill set at M = 4096 and 16384")
     ap.add_argument("--no-small-m", action="store_true",
                     help="skip the smaller prefill batches (M = 512 / 1024 / 2048)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip quantize_gemm_w4a4 against quantize_nvfp4 + gemm_w4a4")
     ap.add_argument("--no-odp", action="store_true",
                     help="skip the host-to-device weight streaming measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -318,6 +320,49 @@ def main():
                 "gemm_frac_fp8_peak": round(fl_all / g_all / 1e9 / PEAK["fp8"], 4),
                 "gemm_frac_f16_peak": round(fl_all / g_all / 1e9 / PEAK["f16"], 4),
                 "quantize_ms": round(q_all, 4), "gemm_ms": round(g_all, 4)}
+        return res
+
+    def fused_vs_two_calls(R, ms, rounds=6, warm=2):
+        """quantize_gemm_w4a4 (quantize folded into the GEMM's activation load)
+        against quantize_nvfp4 + gemm_w4a4 (with its k-split workspace where
+        the shape has one) on the same inputs, interleaved in this process;
+        median per case."""
+        gws = {}
+        for m in ms:
+            for i, r in enumerate(R):
+                nb = qlin.gemm_w4a4_workspace(m, r["L"].n, r["L"].k)
+                gws[(m, i)] = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        t2 = {key: [] for key in gws}
+        tf = {key: [] for key in gws}
+        for rep in range(rounds + warm):
+            for m in ms:
+                for i, r in enumerate(R):
+                    L = r["L"]
+                    e = [E(enable_timing=True) for _ in range(3)]
+                    e[0].record()
+                    qlin.quantize_nvfp4(r["x"][:m], codes=r["codes"][:m], scales=r["scales"][:m],
+                                        workspace=r["ws"], ts_out=r["ts"])
+                    qlin.gemm_w4a4(r["codes"][:m], r["scales"][:m], r["ts"], r["blob"], m, L.n,
+                                   L.k, y=r["y"][:m], workspace=gws[(m, i)])
+                    e[1].record()
+                    qlin.quantize_gemm_w4a4(r["x"][:m], r["blob"], L.n, y=r["y"][:m],
+                                            ts_out=r["ts"], workspace=r["ws"])
+                    e[2].record()
+                    if rep >= warm:
+                        t2[(m, i)].append((e[0], e[1]))
+                        tf[(m, i)].append((e[1], e[2]))
+        torch.cuda.synchronize()
+        res = {}
+        for m in ms:
+            rows, a_all, b_all = [], 0.0, 0.0
+            for i, r in enumerate(R):
+                a = float(np.median([x.elapsed_time(y) for x, y in t2[(m, i)]])) * 1e3
+                b = float(np.median([x.elapsed_time(y) for x, y in tf[(m, i)]])) * 1e3
+                a_all, b_all = a_all + a, b_all + b
+                rows.append({"layer": r["L"].name, "two_calls_us": round(a, 1),
+                             "fused_us": round(b, 1), "fused_speedup": round(a / b, 3)})
+            res[f"m{m}"] = {"layers": rows, "two_calls_us": round(a_all, 1),
+                            "fused_us": round(b_all, 1), "fused_speedup": round(a_all / b_all, 3)}
         return res
 
     # ------------------------------------------------------------ set-up --
@@ -459,6 +504,14 @@ def main():
             qwen.update(interleaved(P, list(SM)))
         qwen["activations"] = ("every row drawn by the seeded generator at M = 8192; smaller M "
                                "are its first rows")
+    fused = {}
+    if P and not args.no_fused:
+        fused = fused_vs_two_calls(P, [16, 64, 128, 512, 2048])
+        fused["timing"] = ("events around quantize_nvfp4 + gemm_w4a4 and around "
+                           "quantize_gemm_w4a4 on the Qwen3-8B-like layers' first M rows, "
+                           "interleaved, median of 6 rounds")
+        _progress("fused quantize + GEMM: " + ", ".join(
+            f"m{m} {fused[f'm{m}']['fused_speedup']}x" for m in (16, 64, 128, 512, 2048)))
 
     # --------------------------------------- decode sweep (MALL defeated) --
     # Each (layer, batch) case is captured once in a HIP graph that launches the
@@ -738,6 +791,7 @@ def main():
             "w4a4_gemm_speedup_vs_bf16": speedup(args.prefill_set, gemm_ms_step * 1e3),
             "prefill_27b": big_parts,
             "prefill_qwen3": qwen,
+            "quantize_gemm_fused_qwen3": fused,
             "w4a4_gemm_speedup_vs_bf16_qwen3_m8192": (
                 speedup("qwen3", sum(l["gemm_us"] for l in qwen["m8192"]["layers"]))
                 if "m8192" in qwen else None),

@@ -34,7 +34,7 @@ SOURCES = {
     "quantize.hip": ["-ffp-contract=off"],
     "weight_prep.hip": ["-ffp-contract=off"],
     "repack.hip": [],
-    "gemm_w4a4.hip": [],
+    "gemm_w4a4.hip": ["-ffp-contract=off"],
     "gemm_w4a4_coop.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
     "gemm_decode.hip": [],
     "gemm_sparse.hip": [],

@@ -192,6 +192,31 @@ int gemm_w4a4_ws(const uint8_t* a_codes, const uint8_t* a_scales, const float* a
                                         as_stream(stream)));
 }
 
+size_t quantize_gemm_w4a4_workspace(int64_t m, int64_t k) {
+  if (m <= 0 || k <= 0 || k % 128 != 0 || k > (int64_t(1) << 20)) return 0;
+  if (m > (int64_t(1) << 31) / 2) return 0;
+  return quantize_nvfp4_workspace(m, k);
+}
+
+int quantize_gemm_w4a4(const void* x_bf16, int64_t m, int64_t k, float* a_tensor_scale,
+                       unsigned flags, const void* w_packed, int64_t n, void* y, int y_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~QL_STATIC_SCALE) return QL_EINVAL;
+  int st = check_gemm(w_packed, y, m, n, k, y_dtype);
+  if (st >= 0) return st;
+  if (!x_bf16 || !a_tensor_scale) return QL_EINVAL;
+  if (!aligned16(x_bf16)) return QL_EALIGN;
+  const bool stat = (flags & QL_STATIC_SCALE) != 0;
+  if (!stat) {
+    if (!workspace) return QL_EINVAL;
+    if (workspace_bytes < quantize_gemm_w4a4_workspace(m, k)) return QL_EWORKSPACE;
+    if (!aligned16(workspace)) return QL_EALIGN;
+  }
+  return launch_status(launch_quantize_gemm_w4a4(x_bf16, m, k, a_tensor_scale, stat,
+                                                 static_cast<uint32_t*>(workspace), w_packed, n,
+                                                 y, y_dtype, as_stream(stream)));
+}
+
 int gemm_w4a16(const void* x_bf16, const void* w_packed, int64_t m, int64_t n, int64_t k,
                void* y, int y_dtype, void* stream) {
   int st = check_gemm(w_packed, y, m, n, k, y_dtype);

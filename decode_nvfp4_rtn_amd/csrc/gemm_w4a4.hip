@@ -45,7 +45,20 @@
 // Block order: tiles are grouped 8 m-tiles wide for L2 reuse, and block ids
 // are remapped so that consecutive tiles land on the same XCD (the hardware
 // deals workgroups round-robin over the 8 XCDs, each with its own L2).
-#include "qlin_internal.hpp"
+//
+// Quantize folded into the activation load (kFuse, quantize_gemm_w4a4): the
+// per-wave kernel can take X itself (bf16) instead of its NVFP4 codes and
+// quantize each k-step's activation tile as it stages it: every thread loads
+// 16-byte vectors of 8 bf16 values (unit v: row v / 16, k 8 (v % 16) of the
+// step), and with its partner lane, which holds the other half of the
+// 16-element group, computes the group's E4M3 scale and the 8 E2M1 codes
+// with the quantizer's own steps (nvfp4_encode.hpp), then writes codes and
+// scale to the same LDS tiles the code loads fill.  The tensor scale comes
+// from the amax pass's partial maxima (each block folds them, as the encode
+// pass does) or is the caller's static scale.  The MFMA work is unchanged,
+// so outputs are bit-identical to quantize_nvfp4 followed by this kernel;
+// the encode is repeated by every block that uses an activation tile.
+#include "nvfp4_encode.hpp"
 
 namespace qlin {
 namespace {
@@ -85,19 +98,40 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int d) {
 }
 
 // WN x WM MFMA tiles (16 x 16 each) per wave; block tile BN x BM with 2 x 2 waves.
-template <int WN, int WM, bool kBF16Out>
+// kFuse: xcodes is X itself (bf16 [M, K]) and xscales is unused; the tensor
+// scale is folded from partial[0 .. npartial) and stored to *ts by block 0,
+// or read from *ts when npartial == 0 (a static scale).  Otherwise xcodes,
+// xscales and a_ts are quantize_nvfp4's outputs.
+template <int WN, int WM, bool kBF16Out, bool kFuse>
 __global__ __launch_bounds__(kThreads) void w4a4_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
-    int64_t ws_off, int M, int N, int K, void* __restrict__ y) {
+    int64_t ws_off, int M, int N, int K, void* __restrict__ y,
+    const uint32_t* __restrict__ partial, int npartial, float* __restrict__ ts) {
   if (!blob_matches(blob, 0, N, K)) return;
   constexpr int BN = 32 * WN, BM = 32 * WM;
   constexpr int WU = BN * 4 / kThreads;   // 16-byte W code units per thread per stage
-  constexpr int XU = BM * 4 / kThreads;   // 16-byte X code units per thread per stage
-  constexpr int SU = (BN + BM + kThreads - 1) / kThreads;  // 8-byte scale rows per thread
+  constexpr int XU = kFuse ? 1 : BM * 4 / kThreads;   // 16-byte X code units per thread per stage
+  constexpr int XB = kFuse ? BM * 16 / kThreads : 1;  // kFuse: 16-byte bf16 X units
+  constexpr int SROWS = kFuse ? BN : BN + BM;         // scale rows loaded from memory
+  constexpr int SU = (SROWS + kThreads - 1) / kThreads;  // 8-byte scale rows per thread
+  static_assert(XB >= 1 && (BM * 16) % kThreads == 0, "activation units");
   __shared__ __attribute__((aligned(16))) uint8_t wc_s[2][BN * RS];
   __shared__ __attribute__((aligned(16))) uint8_t xc_s[2][BM * RS];
   __shared__ __attribute__((aligned(16))) uint8_t sc_s[2][(BN + BM) * 8];
+  __shared__ float inv_tab[kFuse ? 128 : 1];
+  float s_t = 0.0f, d = 0.0f;
+  if constexpr (kFuse) {
+    if (npartial > 0) {
+      s_t = tensor_scale_from_partials<kThreads>(partial, npartial);
+      if (blockIdx.x == 0 && threadIdx.x == 0) *ts = s_t;
+    } else {
+      s_t = *ts;
+    }
+    d = 6.0f * s_t;
+    fill_inv_table(inv_tab, s_t);
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -125,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 pw[WU], px[XU];
+  uint4 pw[WU], px[XU], pxb[XB];
   uint2 ps[SU];
   auto gload = [&](int ks) {
 #pragma unroll
@@ -136,18 +170,29 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
                               wcodes + (int64_t(nt) * KT + ks) * 1024 + (u & 63) * 16)
                         : make_uint4(0, 0, 0, 0);
     }
+    if constexpr (kFuse) {
 #pragma unroll
-    for (int i = 0; i < XU; ++i) {
-      const int u = i * kThreads + tid;
-      const int m = m0 + (u >> 2);
-      px[i] = m < M ? *reinterpret_cast<const uint4*>(xcodes + int64_t(m) * (K / 2) + ks * 64 +
-                                                      (u & 3) * 16)
-                    : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < XB; ++i) {
+        const int v = i * kThreads + tid;
+        const int m = m0 + (v >> 4);
+        pxb[i] = m < M ? *reinterpret_cast<const uint4*>(
+                             xcodes + (int64_t(m) * K + ks * 128 + (v & 15) * 8) * 2)
+                       : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < XU; ++i) {
+        const int u = i * kThreads + tid;
+        const int m = m0 + (u >> 2);
+        px[i] = m < M ? *reinterpret_cast<const uint4*>(xcodes + int64_t(m) * (K / 2) +
+                                                        ks * 64 + (u & 3) * 16)
+                      : make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
-      const int r = i * kThreads + tid;   // 0 .. BN+BM-1; W rows first
-      if (r >= BN + BM) {
+      const int r = i * kThreads + tid;   // 0 .. SROWS-1; W rows first
+      if (r >= SROWS) {
         ps[i] = make_uint2(0, 0);
       } else if (r < BN) {
         const int nt = tn * (BN / 16) + (r >> 4);
@@ -168,14 +213,29 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
       const int wr = (u >> 6) * 16 + ((u & 63) >> 2);
       *reinterpret_cast<uint4*>(&wc_s[buf][wr * RS + (u & 3) * 16]) = pw[i];
     }
+    if constexpr (kFuse) {
+      // quantize the activation tile: a wavefront's 64 units are 4 rows;
+      // rows past M (zeros) are encoded unless the whole wavefront is past M
+      const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-    for (int i = 0; i < XU; ++i) {
-      const int u = i * kThreads + tid;
-      *reinterpret_cast<uint4*>(&xc_s[buf][(u >> 2) * RS + (u & 3) * 16]) = px[i];
+      for (int i = 0; i < XB; ++i) {
+        const int v = i * kThreads + tid;
+        const int row = v >> 4, k8 = v & 15;
+        uint32_t c = 0, sc = 0;
+        if (m0 + ((i * kThreads + wave_u * 64) >> 4) < M) c = encode8_bf16(pxb[i], d, inv_tab, sc);
+        *reinterpret_cast<uint32_t*>(&xc_s[buf][row * RS + k8 * 4]) = c;
+        if ((k8 & 1) == 0) sc_s[buf][(BN + row) * 8 + (k8 >> 1)] = uint8_t(sc);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < XU; ++i) {
+        const int u = i * kThreads + tid;
+        *reinterpret_cast<uint4*>(&xc_s[buf][(u >> 2) * RS + (u & 3) * 16]) = px[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < SU; ++i)
-      if (i * kThreads + tid < BN + BM)
+      if (i * kThreads + tid < SROWS)
         *reinterpret_cast<uint2*>(&sc_s[buf][(i * kThreads + tid) * 8]) = ps[i];
   };
 
@@ -221,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
   }
 
   // epilogue: scale by s_tA * s_tW and store 4 consecutive n per lane
-  const float st = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+  const float st = (kFuse ? s_t : a_ts[0]) * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
 #pragma unroll
   for (int i = 0; i < WN; ++i) {
     const int n = n0 + wn * (BN / 2) + i * 16 + 4 * q;
@@ -243,20 +303,22 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
   }
 }
 
-template <int WN, int WM>
+template <int WN, int WM, bool kFuse = false>
 hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                        const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
-                       int64_t k, void* y, int y_dtype, hipStream_t s) {
+                       int64_t k, void* y, int y_dtype, hipStream_t s,
+                       const uint32_t* partial = nullptr, int npartial = 0,
+                       float* ts = nullptr) {
   constexpr int BN = 32 * WN, BM = 32 * WM;
   const int tiles = static_cast<int>(((m + BM - 1) / BM) * ((n + BN - 1) / BN));
   if (y_dtype == 1)
-    w4a4_kernel<WN, WM, true><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob,
-                                                          L.codes_off, L.aux_off, int(m), int(n),
-                                                          int(k), y);
+    w4a4_kernel<WN, WM, true, kFuse><<<tiles, kThreads, 0, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y,
+        partial, npartial, ts);
   else
-    w4a4_kernel<WN, WM, false><<<tiles, kThreads, 0, s>>>(a_codes, a_scales, a_ts, blob,
-                                                           L.codes_off, L.aux_off, int(m), int(n),
-                                                           int(k), y);
+    w4a4_kernel<WN, WM, false, kFuse><<<tiles, kThreads, 0, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, int(m), int(n), int(k), y,
+        partial, npartial, ts);
   return hipGetLastError();
 }
 
@@ -333,6 +395,29 @@ hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, con
   if (cus > 0 && t128 < cus)
     return launch_tile<2, 2>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
   return launch_tile<4, 4>(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
+}
+
+// Quantize folded into the GEMM: the amax pass (unless the scale is static),
+// then the per-wave kernel quantizing its activation tiles as it stages them,
+// with the tile size launch_gemm_w4a4 gives the per-wave kernel.
+hipError_t launch_quantize_gemm_w4a4(const void* x_bf16, int64_t m, int64_t k, float* ts,
+                                     bool static_scale, uint32_t* partial, const void* w_packed,
+                                     int64_t n, void* y, int y_dtype, hipStream_t s) {
+  const BlobLayout L = blob_layout(0, n, k);
+  const uint8_t* blob = static_cast<const uint8_t*>(w_packed);
+  int npart = 0;
+  if (!static_scale) {
+    hipError_t e = launch_amax_bf16(x_bf16, m, k, partial, &npart, s);
+    if (e != hipSuccess) return e;
+  }
+  const uint8_t* xb = static_cast<const uint8_t*>(x_bf16);
+  const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
+  const int cus = device_cu_count();
+  if (cus > 0 && t128 < cus)
+    return launch_tile<2, 2, true>(xb, nullptr, nullptr, blob, L, m, n, k, y, y_dtype, s, partial,
+                                   npart, ts);
+  return launch_tile<4, 4, true>(xb, nullptr, nullptr, blob, L, m, n, k, y, y_dtype, s, partial,
+                                 npart, ts);
 }
 
 }  // namespace qlin

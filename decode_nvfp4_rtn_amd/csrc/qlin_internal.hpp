@@ -173,6 +173,16 @@ hipError_t launch_quantize_nvfp4(const void* x, int x_dtype, int64_t rows, int64
                                  uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                  bool static_scale, uint32_t* partial, hipStream_t s);
 
+// Pass 1 of the quantizer alone on a bf16 tensor: quantize_blocks(rows, cols)
+// partial maxima (their count is returned in *npartial).
+hipError_t launch_amax_bf16(const void* x, int64_t rows, int64_t cols, uint32_t* partial,
+                            int* npartial, hipStream_t s);
+// The per-wave W4A4 kernel quantizing its activation operand as it loads it
+// (bf16 X; partial: quantize_blocks(m, k) words unless static_scale).
+hipError_t launch_quantize_gemm_w4a4(const void* x_bf16, int64_t m, int64_t k, float* ts,
+                                     bool static_scale, uint32_t* partial, const void* w_packed,
+                                     int64_t n, void* y, int y_dtype, hipStream_t s);
+
 hipError_t launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* codes,
                                 uint16_t* scales, bool prune24, hipStream_t s);
 size_t lut2_workspace(int64_t n, int64_t k);

@@ -52,6 +52,9 @@ _SIGS = {
     "gemm_lut2_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
     "gemm_w4a16_sp24": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp]),
     "gemm_w4a16_sp24_workspace": (_sz, [_i64, _i64, _i64]),
+    "quantize_gemm_w4a4_workspace": (_sz, [_i64, _i64]),
+    "quantize_gemm_w4a4": (_int, [_vp, _i64, _i64, _vp, _uint, _vp, _i64, _vp, _int, _vp, _sz,
+                                  _vp]),
     "gemm_w4a16_sp24_ws": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _int, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -324,6 +327,44 @@ def gemm_w4a4(a_codes, a_scales, a_tensor_scale, w_packed, m, n, k, y=None,
             _ptr(a_codes), _ptr(a_scales), _ptr(a_tensor_scale), _ptr(w_packed), m, n, k,
             _ptr(y), dt, _ptr(workspace), workspace.numel(), _stream(stream)))
     return y
+
+
+def quantize_gemm_w4a4_workspace(m, k):
+    return _lib.quantize_gemm_w4a4_workspace(m, k)
+
+
+def quantize_gemm_w4a4(x, w_packed, n, y=None, out_dtype=torch.float32, tensor_scale=None,
+                       ts_out=None, workspace=None, stream=None):
+    """quantize_nvfp4(x) then gemm_w4a4 in one call whose GEMM quantizes the
+    activation tiles as it loads them (x: bf16 [m, k]).
+
+    tensor_scale: None computes s_t (written to ts_out, allocated when not
+    given); a 1-element fp32 GPU tensor holding a calibrated s_t is used as is
+    (QL_STATIC_SCALE: one launch).  workspace: the amax pass's partial maxima
+    (quantize_gemm_w4a4_workspace(m, k) bytes), allocated when not given.
+    Returns (y, s_t)."""
+    _typed(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError(f"x must be 2-D, got {x.dim()}-D")
+    m, k = x.shape
+    _blob(w_packed, QL_NVFP4, n, k)
+    y, dt = _out(y, m, n, out_dtype, x.device)
+    flags = 0
+    if tensor_scale is None:
+        ts = ts_out if ts_out is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+        _bytes(ts, "ts_out", 4, torch.float32)
+        if workspace is None:
+            workspace = torch.empty(max(16, _lib.quantize_gemm_w4a4_workspace(m, k)),
+                                    dtype=torch.uint8, device=x.device)
+    else:
+        ts = _bytes(tensor_scale, "tensor_scale", 4, torch.float32)
+        flags = QL_STATIC_SCALE
+    if workspace is not None:
+        _typed(workspace, "workspace", torch.uint8)
+    _check("quantize_gemm_w4a4", _lib.quantize_gemm_w4a4(
+        _ptr(x), m, k, _ptr(ts), flags, _ptr(w_packed), n, _ptr(y), dt, _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
+    return y, ts
 
 
 def gemm_w4a16_workspace(m, n, k):

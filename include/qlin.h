@@ -248,6 +248,41 @@ int gemm_w4a4_ws(const uint8_t *a_codes, const uint8_t *a_scales,
                  size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Quantize folded into the W4A4 GEMM (Mix-Quant technical summary, section 2,
+ * system-level deployment: the prefill path quantizes activations to NVFP4
+ * and runs the W4A4 product): the result of quantize_nvfp4 on bf16 X followed
+ * by gemm_w4a4 on its outputs, without materialising the activation codes.
+ * The GEMM kernel quantizes each activation tile as it loads it, with the
+ * quantizer's own operation order (quantize_nvfp4 above), so the codes, the
+ * tensor scale and y are bit-identical to that pair of calls when gemm_w4a4
+ * runs its 128-row-tile kernel (m <= 128, or few 256 x 256 tiles); its
+ * 256 x 256 kernel accumulates each MFMA over another k order and agrees in
+ * fp32 rounding only.  Every block that uses an activation tile quantizes it
+ * again (once per 64 or 128 output columns), so this costs more than the
+ * pair of calls except for small m: the pair stays the faster choice for
+ * large prefill batches.  Two launches (the amax pass, then the GEMM), or one
+ * with a static tensor scale.
+ *
+ * x_bf16          [m, k] bf16, 16-byte aligned.
+ * a_tensor_scale  device fp32 s_t of X: out by default; in when
+ *                 flags & QL_STATIC_SCALE (as quantize_nvfp4).
+ * w_packed        NVFP4 blob of W [n, k] from repack_weights.
+ * y               out [m, n], y_dtype QL_F32 or QL_BF16 (RNE).
+ * workspace       >= quantize_gemm_w4a4_workspace(m, k) bytes of device
+ *                 memory (the amax pass's partial maxima), 16-byte aligned;
+ *                 unused (may be NULL) with QL_STATIC_SCALE.  Calls sharing a
+ *                 workspace must be ordered (same stream).
+ * Shapes: n % 16 == 0, k % 128 == 0, m >= 0.  A blob that is not an NVFP4
+ * blob of this (n, k) leaves y and the tensor scale untouched (as gemm_w4a4).
+ * Errors: QL_EINVAL, QL_ESHAPE, QL_EALIGN, QL_EDTYPE, QL_EWORKSPACE, QL_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t quantize_gemm_w4a4_workspace(int64_t m, int64_t k);
+int quantize_gemm_w4a4(const void *x_bf16, int64_t m, int64_t k, float *a_tensor_scale,
+                       unsigned flags, const void *w_packed, int64_t n, void *y,
+                       int y_dtype, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
  * W4A16 decode GEMV / skinny GEMM (weight-only decode: Disaggregated
  * Quantization; MARLIN article, "どんな技術か": 16-bit activations times
  * INT4 weights, dequantized in registers):

@@ -52,6 +52,8 @@ def lib():
         "gemm_w4a16_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
         "gemm_lut2_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
         "gemm_w4a16_sp24_workspace": (sz, [i64, i64, i64]),
+        "quantize_gemm_w4a4_workspace": (sz, [i64, i64]),
+        "quantize_gemm_w4a4": (i, [vp, i64, i64, vp, u, vp, i64, vp, i, vp, sz, vp]),
         "gemm_w4a16_sp24_ws": (i, [vp, vp, i64, i64, i64, vp, i, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
@@ -68,7 +70,7 @@ def test_header_declares_the_boundary():
     names = set(_declared())
     for n in ("quantize_nvfp4", "repack_weights", "gemm_w4a4", "gemm_w4a16", "gemm_lut2",
               "quantize_int4_g128_sp24", "gemm_w4a16_sp24", "gemm_w4a4_workspace",
-              "gemm_w4a4_ws"):
+              "gemm_w4a4_ws", "quantize_gemm_w4a4", "quantize_gemm_w4a4_workspace"):
         assert n in names
 
 
@@ -162,6 +164,25 @@ def test_decode_ws_validation(lib, fn):
     assert lib.gemm_w4a16_workspace(0, 4096, 12288) == 0
     assert lib.gemm_lut2_workspace(16, 20, 15360) == 0
     assert lib.gemm_w4a16_sp24_workspace(16, 4096, 12000) == 0
+
+
+def test_quantize_gemm_w4a4_validation(lib):
+    g = lib.quantize_gemm_w4a4   # (x, m, k, ts, flags, w, n, y, y_dtype, ws, ws_bytes, stream)
+    assert g(A, 4, 512, B, 0, C, 20, D, 0, E, 4096, None) == QL_ESHAPE      # n % 16
+    assert g(A, 4, 500, B, 0, C, 256, D, 0, E, 4096, None) == QL_ESHAPE     # k % 128
+    assert g(A, 4, 512, B, 0, C, 256, D, 3, E, 4096, None) == QL_EDTYPE
+    assert g(A, 4, 512, B, 2, C, 256, D, 0, E, 4096, None) == QL_EINVAL     # unknown flag
+    assert g(None, 4, 512, B, 0, C, 256, D, 0, E, 4096, None) == QL_EINVAL
+    assert g(A, 4, 512, None, 0, C, 256, D, 0, E, 4096, None) == QL_EINVAL  # no tensor scale
+    assert g(A, 4, 512, B, 0, None, 256, D, 0, E, 4096, None) == QL_EINVAL
+    assert g(A + 8, 4, 512, B, 0, C, 256, D, 0, E, 4096, None) == QL_EALIGN
+    assert g(A, 4, 512, B, 0, C, 256, D, 0, None, 0, None) == QL_EINVAL     # amax needs a workspace
+    assert g(A, 4, 512, B, 0, C, 256, D, 0, E, 0, None) == QL_EWORKSPACE
+    assert g(A, 4, 512, B, 0, C, 256, D, 0, E + 4, 4096, None) == QL_EALIGN
+    assert g(A, -1, 512, B, 0, C, 256, D, 0, E, 4096, None) == QL_EINVAL
+    assert g(None, 0, 512, None, 0, None, 256, None, 0, None, 0, None) == QL_OK   # empty: no-op
+    assert lib.quantize_gemm_w4a4_workspace(0, 512) == 0
+    assert lib.quantize_gemm_w4a4_workspace(8192, 4096) == lib.quantize_nvfp4_workspace(8192, 4096)
 
 
 def test_w4a4_validation(lib):
