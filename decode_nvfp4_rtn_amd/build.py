@@ -10,8 +10,9 @@ into ``decode_nvfp4_rtn_amd/libqlin.so``.  Flags:
   synthesise v_pk_{add,mul,fma}_f32);
 * no fast-math anywhere: divisions stay correctly rounded and denormals are
   kept;
-* ``-ffp-contract=off`` for the quantizers, so no multiply is fused into an
-  add and every binary32 step rounds once;
+* ``-ffp-contract=off`` for the quantizers and for the per-wave W4A4 GEMM,
+  whose fused variant runs the activation encoder, so no multiply is fused
+  into an add and every binary32 step rounds once;
 * the W4A4 block-cooperative GEMM is scheduled with the compiler's
   memory-clause strategy, which keeps its loads and LDS reads in tighter
   groups: 0.5-3.3 % faster over the Qwen3-8B-like and 27B-class prefill
