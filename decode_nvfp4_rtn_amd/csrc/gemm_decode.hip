@@ -117,10 +117,11 @@ __device__ __forceinline__ void load_xfrag(XFrag<MT>& X, const uint16_t* const (
 // fp32 scale multiply-add.  Slots past the wave's range or past k are clamped
 // to a valid address and contribute zero (their scales are replaced by 0),
 // so the loop has no branches and the compiler can count outstanding loads.
-// XQ >= 0 (a wave's groups fit one chunk): the activation rows of all the
-// wave's groups are loaded first and staged with rows_stage (NQ = XQ) once
-// the chunk's weight loads are in flight.
-template <int MT, int NTB, int WMAX, int KWT, int XQ, bool kBF16Out>
+// XQ >= 0: the activation rows of the wave's groups are loaded first and
+// staged with rows_stage (NQ = XQ) once the chunk's weight loads are in
+// flight -- all of them before the loop when they fit one chunk, else
+// (kRowsPerChunk) each chunk's at the top of its iteration.
+template <int MT, int NTB, int WMAX, int KWT, int XQ, bool kBF16Out, bool kRowsPerChunk = false>
 __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restrict__ x,
                                                         const uint8_t* __restrict__ blob,
                                                         int64_t codes_off, int64_t sc_off, int M,
@@ -160,10 +161,12 @@ __global__ __launch_bounds__(KWT * 64) void w4a16_kernel(const uint16_t* __restr
 
   __shared__ __attribute__((aligned(16))) uint8_t xst[XQ >= 0 ? KWT : 1][4096];
   bf16x8_t xpre[XQ >= 0 ? WMAX : 1][4][MT];
-  if constexpr (XQ >= 0) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
+  if constexpr (XQ >= 0 && !kRowsPerChunk) rows_load<WMAX, MT, XQ>(x, M, m0, K, g0, gpw, G, lane, xpre);
 
   uint32_t hdr = 0;   // header words (lane l: word l % 8)
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
+    if constexpr (XQ >= 0 && kRowsPerChunk)
+      rows_load<WMAX, MT, XQ>(x, M, m0, K, g0 + c0, gpw - c0, G, lane, xpre);
     uint4 wv[WMAX][NTB];
     uint2 sv[WMAX][NTB];
 #pragma unroll
@@ -895,7 +898,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   }
 }
 
-template <bool kLut, int MT, int NTB, int WMAX, int KWT, int XQ>
+template <bool kLut, int MT, int NTB, int WMAX, int KWT, int XQ, bool kRowsPerChunk = false>
 hipError_t launch_decode_xq(const void* x, const uint8_t* blob, const BlobLayout& L, int M,
                             int m0, int N, int K, void* y, int y_dtype, hipStream_t s) {
   const int blocks = (N / 16 + NTB - 1) / NTB;
@@ -909,18 +912,19 @@ hipError_t launch_decode_xq(const void* x, const uint8_t* blob, const BlobLayout
           xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
   } else {
     if (y_dtype == 1)
-      w4a16_kernel<MT, NTB, WMAX, KWT, XQ, true><<<blocks, KWT * 64, 0, s>>>(
+      w4a16_kernel<MT, NTB, WMAX, KWT, XQ, true, kRowsPerChunk><<<blocks, KWT * 64, 0, s>>>(
           xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
     else
-      w4a16_kernel<MT, NTB, WMAX, KWT, XQ, false><<<blocks, KWT * 64, 0, s>>>(
+      w4a16_kernel<MT, NTB, WMAX, KWT, XQ, false, kRowsPerChunk><<<blocks, KWT * 64, 0, s>>>(
           xp, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
   }
   return hipGetLastError();
 }
 
-// A wave's groups in one chunk of at most four (K <= 128 KWT WMAX): the
-// activation rows are staged once (XQ = row quads of this pass's tokens, 0
-// for a single token); otherwise fragments are loaded per group (XQ = -1).
+// Chunks of at most four groups: the activation rows are staged (XQ = row
+// quads of this pass's tokens, 0 for a single token) -- once, when a wave's
+// groups fit one chunk, else per chunk (INT4 with two m-tiles: 32-token
+// passes); otherwise fragments are loaded per group (XQ = -1).
 template <bool kLut, int MT, int NTB, int WMAX, int KWT>
 hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L, int M, int m0,
                          int N, int K, void* y, int y_dtype, hipStream_t s) {
@@ -938,6 +942,9 @@ hipError_t launch_decode(const void* x, const uint8_t* blob, const BlobLayout& L
       }
       return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, 4>(x, blob, L, M, m0, N, K, y, y_dtype, s);
     }
+    if constexpr (!kLut && MT == 2)
+      return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, 4, true>(x, blob, L, M, m0, N, K, y,
+                                                                  y_dtype, s);
   }
   return launch_decode_xq<kLut, MT, NTB, WMAX, KWT, -1>(x, blob, L, M, m0, N, K, y, y_dtype, s);
 }
