@@ -3,9 +3,10 @@
 * quantize_int4_g128_sp24: codes and scales bit-exact (every row).
 * repack (QL_INT4_SP24) + gemm_w4a16_sp24: fp32 outputs within 1e-3 of the
   output RMS of the oracle's fp64 product, bf16 outputs by the bf16 rule; every
-  Qwen3-8B-like decode shape and batch, ragged shapes through both kernels
-  (persistent and k-split), and dense (unpruned) codes, which the packer
-  prunes by |q|.
+  Qwen3-8B-like decode shape and batch (also through the workspace entry
+  point, as the benchmark calls it), ragged shapes through both kernels
+  (persistent and k-split) and through the k split over blocks, and dense
+  (unpruned) codes, which the packer prunes by |q|.
 """
 
 import numpy as np
@@ -93,6 +94,15 @@ def test_sp24_qwen3_decode_all_batches(li):
         ref = gemm.w4a16_sp24(xb, rc, rs)
         _check(host_f64(y32), ref, False)
         _check(host_f64(y16), ref, True)
+        # the workspace entry point, as the benchmark calls it (k split over
+        # blocks where the shape has one)
+        nb = q.gemm_w4a16_sp24_workspace(m, n, k)
+        if nb:
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            y16 = q.gemm_w4a16_sp24(dev_bf16(xb), blob, n, k, out_dtype=torch.bfloat16,
+                                    workspace=ws)
+            torch.cuda.synchronize()
+            _check(host_f64(y16), ref, True)
 
 
 @pytest.mark.parametrize("n,k", [(16 * 1031, 3840), (16 * 1537, 2048), (272, 8320), (272, 12288),
