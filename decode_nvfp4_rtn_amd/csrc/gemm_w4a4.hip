@@ -21,14 +21,16 @@
 // Products of dequantized operands are exact in fp32; only the accumulation
 // rounds.  The ceiling of this exact formulation is the dense fp16 MFMA rate.
 //
-// Two kernels share this arithmetic.  The block-cooperative kernel
+// Three kernels share this arithmetic.  The block-cooperative kernel
 // (gemm_w4a4_coop.hip) dequantizes each code once per block into fp16 LDS
 // tiles of 256 x 256; it runs every problem with m > 128 and more 256 x 256
 // tiles than half the CUs (use_coop below), and a smaller problem when the
 // caller's workspace lets its tiles be split along k and the split pays
 // (split_pays: m > 128, or k >= 8192 for problems of at most half a round).
-// Every other problem uses the per-wave kernel below, whose 4x (or, with
-// fewer 128 x 128 tiles than CUs, 16x) smaller tiles keep every CU busy.
+// Batches of up to 32 tokens take the small-batch kernel (w4a4_small_kernel,
+// the decode kernels' k split over waves), and every other problem the
+// per-wave kernel below, whose 4x (or, with fewer 128 x 128 tiles than CUs,
+// 16x) smaller tiles keep every CU busy.
 //
 // Tiling.  Block tile 128 (n) x 128 (m), k-step 128, four waves in 2 x 2,
 // each wave 64 x 64 = 4 x 4 MFMA tiles.  Codes and scales of both operands are
@@ -303,6 +305,169 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
   }
 }
 
+// Small batches (a pass of up to 16 MT tokens): the decode kernels'
+// organisation with NVFP4 operands.  At a few tokens the per-wave kernel's
+// blocks are few and each wave's dequantization chain sets the pace; here a
+// block of 8 waves owns NTB 16-row weight tiles and the waves split k: each
+// lane loads its fragment bytes straight from the blob (row r = l % 16,
+// bytes 16 q .. 16 q + 15 of a 128-k step, q = l / 16, i.e. groups 2q and
+// 2q + 1 -- the per-wave kernel's fragment mapping, read from the blob's
+// [tile][step][16 rows][64 B] order instead of from LDS) and the activation
+// fragments of the same k from the code rows, dequantizes both exactly to
+// fp16 and runs v_mfma_f32_16x16x32_f16; a chunk of WMAX steps' loads is
+// issued at once.  The waves' partial sums meet in LDS in a fixed order, and
+// the tensor scales are applied to the sum, as in the other kernels.  Slots
+// past the wave's range or past k read a clamped step with a zero scale, so
+// they contribute nothing and the loop has no branches around loads.
+constexpr int kSmallWaves = 8;
+// Batches of up to 32 tokens take this kernel: measured against the per-wave
+// kernel on the Qwen3-8B-like and 27B-class layers (interleaved, bf16 out),
+// 1.3-4.3x faster at M = 1-32 (down 4096 x 12288 at M = 1: 18 against 79
+// us); from M = 64 the per-wave kernel's 64- or 128-row tiles, which read
+// each weight once per 64 or 128 tokens, win on the wide and long layers.
+constexpr int64_t kSmallMaxM = 32;
+
+template <int MT, int NTB, int WMAX, bool kBF16Out>
+__global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
+    const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
+    const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
+    int64_t ws_off, int M, int m0, int N, int K, void* __restrict__ y) {
+  if (!blob_matches(blob, 0, N, K)) return;   // before any barrier: uniform
+  constexpr int NW = kSmallWaves;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int r = lane & 15, q = lane >> 4;
+  const int KT = K / 128;
+  const int gpw = (KT + NW - 1) / NW;
+  const int g0 = wave * gpw;
+  const int nt0 = blockIdx.x * NTB;
+  const int NT16 = N / 16;
+
+  const uint8_t* wc[NTB];
+  const uint8_t* wsc[NTB];
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt) {
+    const int64_t tile = min(nt0 + nt, NT16 - 1);
+    wc[nt] = blob + wc_off + tile * KT * 1024 + r * 64 + q * 16;
+    wsc[nt] = blob + ws_off + tile * KT * 128 + r * 8 + 2 * q;
+  }
+  const uint8_t* xc[MT];
+  const uint8_t* xs[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t row = min(m0 + mt * 16 + r, M - 1);   // rows past M: computed, not stored
+    xc[mt] = xcodes + row * (K / 2) + q * 16;
+    xs[mt] = xscales + row * (K / 16) + 2 * q;
+  }
+
+  floatx4 acc[NTB][MT];
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < gpw; c0 += WMAX) {
+    uint4 wv[WMAX][NTB], xv[WMAX][MT];
+    uint32_t wsv[WMAX][NTB], xsv[WMAX][MT];
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      const int g = min(g0 + min(c0 + i, gpw - 1), KT - 1);
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt) {
+        wv[i][nt] = load_nt16(wc[nt] + int64_t(g) * 1024);
+        wsv[i][nt] = *reinterpret_cast<const uint16_t*>(wsc[nt] + int64_t(g) * 128);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        xv[i][mt] = *reinterpret_cast<const uint4*>(xc[mt] + int64_t(g) * 64);
+        xsv[i][mt] = *reinterpret_cast<const uint16_t*>(xs[mt] + int64_t(g) * 8);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // the chunk's loads go out before its arithmetic
+#pragma unroll
+    for (int i = 0; i < WMAX; ++i) {
+      const bool live = c0 + i < gpw && g0 + c0 + i < KT;   // wave-uniform
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {          // d = 2c + s: group 2q + c, half s
+        half8_t xf[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          xf[mt] = dequant8(dword(xv[i][mt], d), scale2(xsv[i][mt], d >> 1));
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt) {
+          const half8_t wf = dequant8(dword(wv[i][nt], d), scale2(live ? wsv[i][nt] : 0u, d >> 1));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf[mt], acc[nt][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // partial sums of the waves -> LDS; sum in wave order, scale, store
+  __shared__ floatx4 red[NW][NTB][MT][64];
+#pragma unroll
+  for (int nt = 0; nt < NTB; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[wave][nt][mt][lane] = acc[nt][mt];
+  __syncthreads();
+  const float st = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+  for (int t = threadIdx.x; t < NTB * MT * 64; t += NW * 64) {
+    const int nt = t / (MT * 64), mt = (t / 64) % MT, ln = t % 64;
+    floatx4 v = red[0][nt][mt][ln];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += red[w][nt][mt][ln];
+    v = v * st;
+    const int n = (nt0 + nt) * 16 + 4 * (ln >> 4);
+    const int m = m0 + mt * 16 + (ln & 15);
+    if (m < M && n < N) {
+      if (kBF16Out) {
+        uint2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
+      } else {
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+      }
+    }
+  }
+}
+
+template <int MT, int NTB>
+hipError_t launch_small_pass(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                             const uint8_t* blob, const BlobLayout& L, int M, int m0, int N,
+                             int K, void* y, int y_dtype, hipStream_t s) {
+  const int blocks = (N / 16 + NTB - 1) / NTB;
+  if (y_dtype == 1)
+    w4a4_small_kernel<MT, NTB, 4, true><<<blocks, kSmallWaves * 64, 0, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
+  else
+    w4a4_small_kernel<MT, NTB, 4, false><<<blocks, kSmallWaves * 64, 0, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
+  return hipGetLastError();
+}
+
+// passes of up to 32 tokens (two m-tiles), two row tiles per block when that
+// still leaves at least 192 blocks
+hipError_t launch_small_all(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                            const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
+                            int64_t k, void* y, int y_dtype, hipStream_t s) {
+  const bool wide = n / 16 >= 384;
+  for (int64_t m0 = 0; m0 < m; m0 += 32) {
+    const int rows = int(m - m0 < 32 ? m - m0 : 32);
+    const int M = int(m), M0 = int(m0), N = int(n), K = int(k);
+    hipError_t e;
+    if (rows <= 16)
+      e = wide ? launch_small_pass<1, 2>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s)
+               : launch_small_pass<1, 1>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s);
+    else
+      e = wide ? launch_small_pass<2, 2>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s)
+               : launch_small_pass<2, 1>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int WN, int WM, bool kFuse = false>
 hipError_t launch_tile(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                        const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
@@ -357,7 +522,10 @@ bool use_coop(int64_t m, int64_t n, int64_t k) {
 // MFMA work) unless k is long.  Measured over the Qwen3-8B-like and 27B-class
 // shapes at m = 128-2048: the split ran 0.80-0.99x at m = 128 with k <= 5120,
 // 1.47-1.58x there with k >= 12288, and 0.93-1.99x (mostly > 1) at m >= 256.
+// Batches the small-batch kernel takes are never split: it ran 2.9-3.7x the
+// per-wave kernel on down 4096 x 12288 at M = 16-32, the split at most 1.6x.
 bool split_pays(int64_t m, int64_t n, int64_t k) {
+  if (m <= kSmallMaxM) return false;
   const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
   const int cus = device_cu_count();
   if (cus > 0 && big_tiles * 2 <= cus) return m > 128 || k >= 8192;
@@ -386,6 +554,8 @@ hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, con
   if (split || use_coop(m, n, k))
     return launch_gemm_w4a4_coop(a_codes, a_scales, a_ts, w_packed, m, n, k, y, y_dtype,
                                  static_cast<float*>(ws), split, s);
+  if (m <= kSmallMaxM)
+    return launch_small_all(a_codes, a_scales, a_ts, blob, L, m, n, k, y, y_dtype, s);
   // With fewer 128x128 tiles than CUs, 64x64 tiles (4x the blocks) fill the
   // chip better despite twice the dequantization per product: 1.07-1.87x at
   // M = 64-512 on the Qwen3-8B-like shapes (outputs bit-identical: every

@@ -3,9 +3,10 @@ GEMM's activation load).
 
 * Against the two-call path on the same inputs: quantize_nvfp4 on bf16 X,
   then gemm_w4a4 without a workspace.  Where gemm_w4a4 runs its 128-row-tile
-  kernel (m <= 128, or few 256 x 256 tiles) the outputs and the tensor scale
-  must be bit-identical; the 256 x 256 kernel accumulates each MFMA over
-  another k order, so there only the tensor scale is compared exactly.
+  kernel (32 < m <= 128, or few 256 x 256 tiles) the outputs and the tensor
+  scale must be bit-identical; its small-batch and 256 x 256 kernels
+  accumulate in another k order, so there only the tensor scale is compared
+  exactly.
 * Against the oracle (its own quantization of X and W, fp64 product): the
   fp32 and bf16 output bars of the other W4A4 tests, and the tensor scale
   bit for bit.
@@ -48,10 +49,12 @@ def _two_calls(q, x, blob, n, dt, ts=None):
 
 
 def _per_wave(m, n):
-    """gemm_w4a4 (no workspace) runs the 128-row-tile kernel on this shape."""
+    """gemm_w4a4 (no workspace) runs the 128-row-tile kernel on this shape
+    (batches of up to 32 tokens take the small-batch kernel, whose k order
+    differs)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     big = ((m + 255) // 256) * ((n + 255) // 256)
-    return m <= 128 or 2 * big <= cus
+    return m > 32 and (m <= 128 or 2 * big <= cus)
 
 
 # m: one token, a partial first wavefront, ragged 64- and 128-row tiles;

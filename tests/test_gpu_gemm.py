@@ -87,6 +87,32 @@ def test_w4a4_ragged(m, n, k):
         _check(host_f64(y), ref, dt == torch.bfloat16)
 
 
+# Batches of up to 32 tokens take the small-batch kernel (waves split k, one
+# or two 16-row tiles and one or two m-tiles per block): one and two m-tiles
+# with ragged rows, one row tile per block and two (N >= 6144, odd tile
+# count), k from one step (idle waves) to several chunks per wave, both
+# output dtypes; and the workspace call, which never splits these batches.
+@pytest.mark.parametrize("n,k", [(256, 128), (4112, 640), (6160, 4096), (272, 12288),
+                                 (6144, 4224)])
+def test_w4a4_small_batches(n, k):
+    q = require_gpu()
+    w = synth.weights(19, n, n, k)
+    say("w4a4 small batches", n, k)
+    blob = _nvfp4_blob(q, w)
+    wq = nvfp4.quantize(w)
+    del w
+    for m in (1, 7, 16, 17, 31, 32):
+        x = synth.activations(19, m, m, k, outliers="channels")
+        ac, as_, at = q.quantize_nvfp4(dev_f32(x))
+        assert q.gemm_w4a4_workspace(m, n, k) == 0
+        y32 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.float32)
+        y16 = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        ref = gemm.w4a4(*nvfp4.quantize(x), *wq)
+        _check(host_f64(y32), ref, False)
+        _check(host_f64(y16), ref, True)
+
+
 # One prefill layer at a time: the oracle's quantization of its weights (every
 # row), its GPU blob, and the activations at the largest M of the case list
 # (smaller M are their first rows, as the seeded draw is by 256-row block).
