@@ -327,13 +327,32 @@ constexpr int kSmallWaves = 8;
 // each weight once per 64 or 128 tokens, win on the wide and long layers.
 constexpr int64_t kSmallMaxM = 32;
 
-template <int MT, int NTB, int WMAX, bool kBF16Out>
+// kFuse: xcodes is X itself (bf16 [M, K]) and xscales is unused; each lane
+// loads its two groups' 32 bf16 values of a step and encodes them whole
+// (encode16_bf16, the quantizer's steps), with the tensor scale folded from
+// partial[0 .. npartial) (block 0 stores it to *ts) or read from *ts.
+template <int MT, int NTB, int WMAX, bool kBF16Out, bool kFuse = false>
 __global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const float* __restrict__ a_ts, const uint8_t* __restrict__ blob, int64_t wc_off,
-    int64_t ws_off, int M, int m0, int N, int K, void* __restrict__ y) {
+    int64_t ws_off, int M, int m0, int N, int K, void* __restrict__ y,
+    const uint32_t* __restrict__ partial = nullptr, int npartial = 0,
+    float* __restrict__ ts = nullptr) {
   if (!blob_matches(blob, 0, N, K)) return;   // before any barrier: uniform
   constexpr int NW = kSmallWaves;
+  __shared__ float inv_tab[kFuse ? 128 : 1];
+  float s_t = 0.0f, d6 = 0.0f;
+  if constexpr (kFuse) {
+    if (npartial > 0) {
+      s_t = tensor_scale_from_partials<NW * 64>(partial, npartial);
+      if (blockIdx.x == 0 && threadIdx.x == 0 && m0 == 0) *ts = s_t;
+    } else {
+      s_t = *ts;
+    }
+    d6 = 6.0f * s_t;
+    fill_inv_table(inv_tab, s_t);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int r = lane & 15, q = lane >> 4;
@@ -356,8 +375,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int64_t row = min(m0 + mt * 16 + r, M - 1);   // rows past M: computed, not stored
-    xc[mt] = xcodes + row * (K / 2) + q * 16;
-    xs[mt] = xscales + row * (K / 16) + 2 * q;
+    if constexpr (kFuse) {
+      xc[mt] = xcodes + (row * K + q * 32) * 2;          // bf16 elements 32 q .. of a step
+      xs[mt] = nullptr;
+    } else {
+      xc[mt] = xcodes + row * (K / 2) + q * 16;
+      xs[mt] = xscales + row * (K / 16) + 2 * q;
+    }
   }
 
   floatx4 acc[NTB][MT];
@@ -369,6 +393,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
   for (int c0 = 0; c0 < gpw; c0 += WMAX) {
     uint4 wv[WMAX][NTB], xv[WMAX][MT];
     uint32_t wsv[WMAX][NTB], xsv[WMAX][MT];
+    uint4 xb[kFuse ? WMAX : 1][kFuse ? MT : 1][4];
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
       const int g = min(g0 + min(c0 + i, gpw - 1), KT - 1);
@@ -379,11 +404,30 @@ __global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        xv[i][mt] = *reinterpret_cast<const uint4*>(xc[mt] + int64_t(g) * 64);
-        xsv[i][mt] = *reinterpret_cast<const uint16_t*>(xs[mt] + int64_t(g) * 8);
+        if constexpr (kFuse) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            xb[i][mt][u] = *reinterpret_cast<const uint4*>(xc[mt] + int64_t(g) * 256 + u * 16);
+        } else {
+          xv[i][mt] = *reinterpret_cast<const uint4*>(xc[mt] + int64_t(g) * 64);
+          xsv[i][mt] = *reinterpret_cast<const uint16_t*>(xs[mt] + int64_t(g) * 8);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);   // the chunk's loads go out before its arithmetic
+    if constexpr (kFuse) {
+      // the lane's two groups (2q, 2q + 1) of each step, encoded whole
+#pragma unroll
+      for (int i = 0; i < WMAX; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          uint32_t c[4], s0, s1;
+          encode16_bf16(xb[i][mt][0], xb[i][mt][1], d6, inv_tab, c[0], c[1], s0);
+          encode16_bf16(xb[i][mt][2], xb[i][mt][3], d6, inv_tab, c[2], c[3], s1);
+          xv[i][mt] = make_uint4(c[0], c[1], c[2], c[3]);
+          xsv[i][mt] = s0 | (s1 << 8);
+        }
+    }
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
       const bool live = c0 + i < gpw && g0 + c0 + i < KT;   // wave-uniform
@@ -411,7 +455,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) red[wave][nt][mt][lane] = acc[nt][mt];
   __syncthreads();
-  const float st = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+  const float st = (kFuse ? s_t : a_ts[0]) * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
   for (int t = threadIdx.x; t < NTB * MT * 64; t += NW * 64) {
     const int nt = t / (MT * 64), mt = (t / 64) % MT, ln = t % 64;
     floatx4 v = red[0][nt][mt][ln];
@@ -433,36 +477,46 @@ __global__ __launch_bounds__(kSmallWaves * 64) void w4a4_small_kernel(
   }
 }
 
-template <int MT, int NTB>
+template <int MT, int NTB, bool kFuse = false>
 hipError_t launch_small_pass(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                              const uint8_t* blob, const BlobLayout& L, int M, int m0, int N,
-                             int K, void* y, int y_dtype, hipStream_t s) {
+                             int K, void* y, int y_dtype, hipStream_t s,
+                             const uint32_t* partial = nullptr, int npartial = 0,
+                             float* ts = nullptr) {
+  constexpr int WMAX = kFuse ? 2 : 4;   // the bf16 rows of a chunk take 4x the registers of codes
   const int blocks = (N / 16 + NTB - 1) / NTB;
   if (y_dtype == 1)
-    w4a4_small_kernel<MT, NTB, 4, true><<<blocks, kSmallWaves * 64, 0, s>>>(
-        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
+    w4a4_small_kernel<MT, NTB, WMAX, true, kFuse><<<blocks, kSmallWaves * 64, 0, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, M, m0, N, K, y, partial, npartial,
+        ts);
   else
-    w4a4_small_kernel<MT, NTB, 4, false><<<blocks, kSmallWaves * 64, 0, s>>>(
-        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, M, m0, N, K, y);
+    w4a4_small_kernel<MT, NTB, WMAX, false, kFuse><<<blocks, kSmallWaves * 64, 0, s>>>(
+        a_codes, a_scales, a_ts, blob, L.codes_off, L.aux_off, M, m0, N, K, y, partial, npartial,
+        ts);
   return hipGetLastError();
 }
 
 // passes of up to 32 tokens (two m-tiles), two row tiles per block when that
 // still leaves at least 192 blocks
+template <bool kFuse = false>
 hipError_t launch_small_all(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                             const uint8_t* blob, const BlobLayout& L, int64_t m, int64_t n,
-                            int64_t k, void* y, int y_dtype, hipStream_t s) {
+                            int64_t k, void* y, int y_dtype, hipStream_t s,
+                            const uint32_t* partial = nullptr, int npartial = 0,
+                            float* ts = nullptr) {
   const bool wide = n / 16 >= 384;
   for (int64_t m0 = 0; m0 < m; m0 += 32) {
     const int rows = int(m - m0 < 32 ? m - m0 : 32);
     const int M = int(m), M0 = int(m0), N = int(n), K = int(k);
     hipError_t e;
+#define QL_SMALL(MT, NTB)                                                                    \
+  launch_small_pass<MT, NTB, kFuse>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, \
+                                    s, partial, npartial, ts)
     if (rows <= 16)
-      e = wide ? launch_small_pass<1, 2>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s)
-               : launch_small_pass<1, 1>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s);
+      e = wide ? QL_SMALL(1, 2) : QL_SMALL(1, 1);
     else
-      e = wide ? launch_small_pass<2, 2>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s)
-               : launch_small_pass<2, 1>(a_codes, a_scales, a_ts, blob, L, M, M0, N, K, y, y_dtype, s);
+      e = wide ? QL_SMALL(2, 2) : QL_SMALL(2, 1);
+#undef QL_SMALL
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -568,8 +622,9 @@ hipError_t launch_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, con
 }
 
 // Quantize folded into the GEMM: the amax pass (unless the scale is static),
-// then the per-wave kernel quantizing its activation tiles as it stages them,
-// with the tile size launch_gemm_w4a4 gives the per-wave kernel.
+// then the small-batch kernel (m <= 32) or the per-wave kernel quantizing the
+// activation as they load it, with the kernel and tile size launch_gemm_w4a4
+// gives that batch without a workspace (so results match it bit for bit).
 hipError_t launch_quantize_gemm_w4a4(const void* x_bf16, int64_t m, int64_t k, float* ts,
                                      bool static_scale, uint32_t* partial, const void* w_packed,
                                      int64_t n, void* y, int y_dtype, hipStream_t s) {
@@ -581,6 +636,9 @@ hipError_t launch_quantize_gemm_w4a4(const void* x_bf16, int64_t m, int64_t k, f
     if (e != hipSuccess) return e;
   }
   const uint8_t* xb = static_cast<const uint8_t*>(x_bf16);
+  if (m <= kSmallMaxM)
+    return launch_small_all<true>(xb, nullptr, nullptr, blob, L, m, n, k, y, y_dtype, s, partial,
+                                  npart, ts);
   const int64_t t128 = ((m + 127) / 128) * ((n + 127) / 128);
   const int cus = device_cu_count();
   if (cus > 0 && t128 < cus)

@@ -125,4 +125,34 @@ __device__ __forceinline__ uint32_t encode8_bf16(const uint4& t, float d, const 
   return e2m1_pack8(y);
 }
 
+// A whole 16-element group of bf16 values held by one lane (a: elements
+// 0..7, b: 8..15, element 2j in the low half of dword j): the same steps as
+// encode8_bf16, the two halves' maxima combined with the same fmaxf that
+// combines the two lanes' there (so NaN inputs give the same scale).
+// Returns the 16 E2M1 codes in two dwords (c0: elements 0..7, c1: 8..15)
+// and sets sc to the E4M3 scale code.
+__device__ __forceinline__ void encode16_bf16(const uint4& a, const uint4& b, float d,
+                                              const float* inv_tab, uint32_t& c0, uint32_t& c1,
+                                              uint32_t& sc) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  auto half_max = [&](int h) {
+    qlin_u16x2 mx = __builtin_bit_cast(qlin_u16x2, w[4 * h] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      mx = __builtin_elementwise_max(mx, __builtin_bit_cast(qlin_u16x2, w[4 * h + j] & 0x7FFF7FFFu));
+    return __uint_as_float(uint32_t(mx[0] > mx[1] ? mx[0] : mx[1]) << 16);
+  };
+  const float amax = __builtin_fmaxf(half_max(0), half_max(1));
+  sc = (d == 0.0f) ? 0u : enc_e4m3(amax / d);
+  const float inv = inv_tab[sc];
+  float y[2][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    y[j >> 2][2 * (j & 3)] = __uint_as_float(w[j] << 16) * inv;
+    y[j >> 2][2 * (j & 3) + 1] = __uint_as_float(w[j] & 0xFFFF0000u) * inv;
+  }
+  c0 = e2m1_pack8(y[0]);
+  c1 = e2m1_pack8(y[1]);
+}
+
 }  // namespace qlin

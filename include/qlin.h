@@ -254,15 +254,17 @@ int gemm_w4a4_ws(const uint8_t *a_codes, const uint8_t *a_scales,
  * by gemm_w4a4 on its outputs, without materialising the activation codes.
  * The GEMM kernel quantizes each activation tile as it loads it, with the
  * quantizer's own operation order (quantize_nvfp4 above), so the codes, the
- * tensor scale and y are bit-identical to that pair of calls when gemm_w4a4
- * runs its 128-row-tile kernel (32 < m <= 128, or few 256 x 256 tiles); its
- * small-batch and 256 x 256 kernels accumulate in another k order and agree
- * in fp32 rounding only.  Every block that uses an activation tile quantizes
- * it again (once per 64 or 128 output columns), so this costs more than the
- * pair of calls at every batch size measured; it is for callers that want
- * no activation codes in memory, or a single launch with a static tensor
- * scale.  Two launches (the amax pass, then the GEMM), or one with a static
- * tensor scale.
+ * tensor scale and y are bit-identical to that pair of calls wherever
+ * gemm_w4a4 runs its small-batch kernel (m <= 32) or its 128-row-tile kernel
+ * (m <= 128, or few 256 x 256 tiles), whose quantizing variants this call
+ * runs; gemm_w4a4's 256 x 256 kernel accumulates in another k order and
+ * agrees in fp32 rounding only.  Every block that uses an activation group
+ * quantizes it again (once per block of output columns): at m <= 32 this
+ * costs about as much as the pair of calls (less on narrow layers), above
+ * that about twice as much.  It is for callers that want no activation
+ * codes in memory, or a single launch with a static tensor scale.  Two
+ * launches (the amax pass, then the GEMM), or one with a static tensor
+ * scale.
  *
  * x_bf16          [m, k] bf16, 16-byte aligned.
  * a_tensor_scale  device fp32 s_t of X: out by default; in when

@@ -2,11 +2,12 @@
 GEMM's activation load).
 
 * Against the two-call path on the same inputs: quantize_nvfp4 on bf16 X,
-  then gemm_w4a4 without a workspace.  Where gemm_w4a4 runs its 128-row-tile
-  kernel (32 < m <= 128, or few 256 x 256 tiles) the outputs and the tensor
-  scale must be bit-identical; its small-batch and 256 x 256 kernels
-  accumulate in another k order, so there only the tensor scale is compared
-  exactly.
+  then gemm_w4a4 without a workspace.  Where gemm_w4a4 runs the kernel whose
+  quantizing variant this call runs -- the small-batch kernel (m <= 32) or
+  the 128-row-tile kernel (m <= 128, or few 256 x 256 tiles) -- the outputs
+  and the tensor scale must be bit-identical; its 256 x 256 kernel
+  accumulates each MFMA over another k order, so there only the tensor scale
+  is compared exactly.
 * Against the oracle (its own quantization of X and W, fp64 product): the
   fp32 and bf16 output bars of the other W4A4 tests, and the tensor scale
   bit for bit.
@@ -48,18 +49,21 @@ def _two_calls(q, x, blob, n, dt, ts=None):
     return q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=dt), at
 
 
-def _per_wave(m, n):
-    """gemm_w4a4 (no workspace) runs the 128-row-tile kernel on this shape
-    (batches of up to 32 tokens take the small-batch kernel, whose k order
-    differs)."""
+def _same_kernel(m, n):
+    """gemm_w4a4 (no workspace) runs, on this shape, the kernel whose
+    quantizing variant quantize_gemm_w4a4 runs: the small-batch kernel
+    (m <= 32) or the 128-row-tile kernel (m <= 128, or few 256 x 256 tiles)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     big = ((m + 255) // 256) * ((n + 255) // 256)
-    return m > 32 and (m <= 128 or 2 * big <= cus)
+    return m <= 128 or 2 * big <= cus
 
 
-# m: one token, a partial first wavefront, ragged 64- and 128-row tiles;
-# n: 64 x 64 tiles (fewer 128 x 128 tiles than CUs) and 128 x 128 tiles
+# m: one token, two m-tiles of the small-batch kernel, a partial first
+# wavefront, ragged 64- and 128-row tiles; n: one and two row tiles per
+# small-batch block, 64 x 64 tiles (fewer 128 x 128 tiles than CUs) and
+# 128 x 128 tiles
 @pytest.mark.parametrize("m,n,k", [(1, 256, 512), (3, 4096, 1024), (16, 6144, 4096),
+                                   (29, 6160, 12288), (32, 272, 640),
                                    (61, 272, 640), (100, 12288, 1024), (128, 4096, 4096),
                                    (300, 4096, 1024), (1000, 4112, 640), (2048, 6144, 1024)])
 def test_fused_matches_two_calls_and_oracle(m, n, k):
@@ -74,7 +78,7 @@ def test_fused_matches_two_calls_and_oracle(m, n, k):
         y2, ts2 = _two_calls(q, x, blob, n, dt)
         torch.cuda.synchronize()
         assert torch.equal(ts, ts2)
-        if _per_wave(m, n):
+        if _same_kernel(m, n):
             assert torch.equal(y, y2), dt
         rows = sample_rows(m, 256, m + n)
         xf = orows.bf16_as_f32(bits)
@@ -128,7 +132,7 @@ def test_fused_qwen3_layers_small_batches(li):
         y2, ts2 = _two_calls(q, x, blob, n, torch.bfloat16)
         torch.cuda.synchronize()
         assert torch.equal(ts, ts2)
-        if _per_wave(m, n):
+        if _same_kernel(m, n):
             assert torch.equal(y, y2)
         rows = sample_rows(m, 64, 3 * m + li)
         xf = orows.bf16_as_f32(bits)
