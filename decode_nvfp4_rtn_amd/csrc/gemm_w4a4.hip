@@ -59,7 +59,10 @@
 // from the amax pass's partial maxima (each block folds them, as the encode
 // pass does) or is the caller's static scale.  The MFMA work is unchanged,
 // so outputs are bit-identical to quantize_nvfp4 followed by this kernel;
-// the encode is repeated by every block that uses an activation tile.
+// the encode is repeated by every block that uses an activation tile.  The
+// small-batch kernel has the same variant: each lane loads the 32 bf16
+// values of its two groups in a k-step and encodes each group whole
+// (encode16_bf16), so it needs no partner lane.
 #include "nvfp4_encode.hpp"
 
 namespace qlin {
