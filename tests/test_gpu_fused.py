@@ -13,7 +13,8 @@ GEMM's activation load).
   bit for bit.
 * A static tensor scale (one launch), ragged m (rows past m in a 64- or
   128-row tile, a wavefront whose rows all lie past m), both tile sizes, and
-  a wrong blob, which leaves y and the tensor scale untouched.
+  a wrong blob, which leaves y and the tensor scale untouched; the static
+  scale and the wrong blob through the small-batch kernel as well.
 """
 
 import numpy as np
@@ -88,16 +89,18 @@ def test_fused_matches_two_calls_and_oracle(m, n, k):
         _check(rows_f64(y, rows), ref, dt == torch.bfloat16)
 
 
-def test_fused_static_scale():
-    """A calibrated tensor scale (QL_STATIC_SCALE): one launch, read not written."""
+@pytest.mark.parametrize("m", [77, 20])
+def test_fused_static_scale(m):
+    """A calibrated tensor scale (QL_STATIC_SCALE): one launch, read not
+    written; the per-wave kernel (m = 77) and the small-batch kernel (m = 20)."""
     q = require_gpu()
-    m, n, k = 77, 4096, 2048
+    n, k = 4096, 2048
     bits = synth.activations_bf16(22, 0, m, k, outliers="channels")
     w = synth.weights(22, 1, n, k)
     blob = _nvfp4_blob(q, w)
     x = dev_bf16(bits)
     xf = orows.bf16_as_f32(bits)
-    say("quantize_gemm_w4a4 static scale")
+    say("quantize_gemm_w4a4 static scale", m)
     # a scale below the data's (codes saturate at 6 x 448) and one above it
     for st in (np.float32(nvfp4.tensor_scale(xf) * np.float32(0.37)),
                np.float32(nvfp4.tensor_scale(xf) * np.float32(3.0))):
@@ -141,9 +144,12 @@ def test_fused_qwen3_layers_small_batches(li):
         _check(rows_f64(y, rows), ref, True)
 
 
-def test_fused_blob_guard_and_empty():
+@pytest.mark.parametrize("m", [40, 12])
+def test_fused_blob_guard_and_empty(m):
+    """A wrong blob leaves y and the tensor scale untouched (per-wave kernel
+    at m = 40, small-batch kernel at m = 12); m = 0 is a no-op."""
     q = require_gpu()
-    m, n, k = 40, 256, 512
+    n, k = 256, 512
     w = synth.weights(23, 0, n, k)
     c4, s4 = q.quantize_int4_g128(dev_f32(w))
     i4 = q.repack_weights(q.QL_INT4_G128, n, k, c4, s4)
@@ -151,7 +157,7 @@ def test_fused_blob_guard_and_empty():
     wrong = torch.zeros_like(right)
     wrong[: min(i4.numel(), wrong.numel())] = i4[: min(i4.numel(), wrong.numel())]
     x = dev_bf16(synth.activations_bf16(23, 1, m, k))
-    say("quantize_gemm_w4a4 blob guard")
+    say("quantize_gemm_w4a4 blob guard", m)
     y = torch.full((m, n), 7.0, dtype=torch.float32, device="cuda")
     ts = torch.full((1,), 5.0, dtype=torch.float32, device="cuda")
     q.quantize_gemm_w4a4(x, wrong, n, y=y, ts_out=ts)
