@@ -271,22 +271,48 @@ __global__ __launch_bounds__(WAVES * 64, 1) void w4a4_coop_kernel(
     return;
   }
   const float stv = a_ts[0] * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+  if constexpr (kBF16Out) {
+    // The accumulators hold 4 consecutive columns of one row per lane, so a
+    // direct store instruction writes 16 rows x 32 bytes: every 128-byte line
+    // of the output is written in four partial pieces.  Each wave instead
+    // passes its 128 (n) x 64 (m) bf16 tile through a private LDS region
+    // (row-major, 288-byte rows: conflict-free 8-byte writes and 16-byte
+    // reads) and stores whole rows, 4 rows x 256 bytes per instruction.  LDS
+    // is idle here (every wave has passed the last stage's barrier), and one
+    // wave's LDS operations complete in order, so no barrier is needed.
+    constexpr int ORS = 288;
+    static_assert(WAVES * TM * 16 * ORS <= 2 * 2 * TILE_BYTES, "output staging fits in LDS");
+    uint8_t* const ot = smem + wave * (TM * 16 * ORS);
 #pragma unroll
-  for (int i = 0; i < TN; ++i) {
-    const int n = n0 + wn * 128 + i * 16 + 4 * q;
-    if (n >= N) continue;
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int m = m0 + wm * (TM * 16) + j * 16 + r;
-      if (m >= M) continue;
-      const floatx4 v = acc[i][j] * stv;
-      if (kBF16Out) {
+      for (int j = 0; j < TM; ++j) {
+        const floatx4 v = acc[i][j] * stv;
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
-      } else {
-        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+        *reinterpret_cast<uint2*>(ot + (16 * j + r) * ORS + (16 * i + 4 * q) * 2) = o;
+      }
+    __asm__ volatile("" ::: "memory");   // keep the reads below the writes
+    const int n = n0 + wn * 128 + 8 * (lane & 15);
+#pragma unroll
+    for (int it = 0; it < TM * 4; ++it) {
+      const int rr = 4 * it + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(ot + rr * ORS + 16 * (lane & 15));
+      const int m = m0 + wm * (TM * 16) + rr;
+      if (m < M && n < N)   // N is a multiple of 16: a lane's 8 columns are all in or all out
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int n = n0 + wn * 128 + i * 16 + 4 * q;
+      if (n >= N) continue;
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int m = m0 + wm * (TM * 16) + j * 16 + r;
+        if (m >= M) continue;
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = acc[i][j] * stv;
       }
     }
   }
