@@ -285,24 +285,53 @@ __global__ __launch_bounds__(kThreads) void w4a4_kernel(
     __syncthreads();
   }
 
-  // epilogue: scale by s_tA * s_tW and store 4 consecutive n per lane
+  // epilogue: scale by s_tA * s_tW.  The accumulators hold 4 consecutive n of
+  // one row per lane, so a direct bf16 store instruction writes 16 rows x 32
+  // bytes, each output line in several partial pieces; bf16 tiles are
+  // instead staged per wave in LDS (the code tiles are idle after the last
+  // barrier; row stride 32 WN + 16 bytes: conflict-free 8-byte writes) and
+  // stored as whole wave rows, 64 / (2 WN) rows of 32 WN bytes per
+  // instruction.  One wave's LDS operations complete in order: no barrier.
   const float st = (kFuse ? s_t : a_ts[0]) * reinterpret_cast<const BlobHeader*>(blob)->tensor_scale;
+  if constexpr (kBF16Out) {
+    constexpr int RB = 32 * WN;            // bytes of one wave row (16 WN columns)
+    constexpr int ORS = RB + 16;
+    constexpr int WBYTES = 16 * WM * ORS;  // one wave's staging tile
+    static_assert(2 * WBYTES <= 2 * BN * RS && 2 * WBYTES <= 2 * BM * RS, "staging fits");
+    uint8_t* const ot = (wave < 2 ? &wc_s[0][0] : &xc_s[0][0]) + (wave & 1) * WBYTES;
 #pragma unroll
-  for (int i = 0; i < WN; ++i) {
-    const int n = n0 + wn * (BN / 2) + i * 16 + 4 * q;
-    if (n >= N) continue;
+    for (int i = 0; i < WN; ++i)
 #pragma unroll
-    for (int j = 0; j < WM; ++j) {
-      const int m = m0 + wm * (BM / 2) + j * 16 + r;
-      if (m >= M) continue;
-      const floatx4 v = acc[i][j] * st;
-      if (kBF16Out) {
+      for (int j = 0; j < WM; ++j) {
+        const floatx4 v = acc[i][j] * st;
         uint2 o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = o;
-      } else {
-        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = v;
+        *reinterpret_cast<uint2*>(ot + (16 * j + r) * ORS + (16 * i + 4 * q) * 2) = o;
+      }
+    __asm__ volatile("" ::: "memory");   // keep the reads below the writes
+    constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;          // rows per store instruction
+    const int c = lane % CPR;
+    const int n = n0 + wn * (BN / 2) + 8 * c;
+#pragma unroll
+    for (int it = 0; it < 16 * WM / RPI; ++it) {
+      const int rr = RPI * it + lane / CPR;
+      const uint4 v = *reinterpret_cast<const uint4*>(ot + rr * ORS + 16 * c);
+      const int m = m0 + wm * (BM / 2) + rr;
+      if (m < M && n < N)   // N is a multiple of 16: a lane's 8 columns are all in or all out
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + int64_t(m) * N + n) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int n = n0 + wn * (BN / 2) + i * 16 + 4 * q;
+      if (n >= N) continue;
+#pragma unroll
+      for (int j = 0; j < WM; ++j) {
+        const int m = m0 + wm * (BM / 2) + j * 16 + r;
+        if (m >= M) continue;
+        *reinterpret_cast<floatx4*>(static_cast<float*>(y) + int64_t(m) * N + n) = acc[i][j] * st;
       }
     }
   }
