@@ -665,30 +665,53 @@ def main():
     # M = 8192 (TFLOP/s), and decode GEMV at M = 1 and 16 (GB/s, weights
     # rotated over > 600 MB like the decode sweep).
     bf16_ref = {}
+    same_loop = {}
     if not args.no_bf16_reference:
         sets = (("qwen3", P, 8192),) if args.prefill_set == "qwen3" else \
             (("27b", R, M), ("qwen3", P, 8192))
         for tag, S, m in sets:
+            tot_b = tot_w = 0.0
             for r in S:
                 L = r["L"]
                 wb = torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev) * (L.k ** -0.5)
                 yb = torch.empty((m, L.n), dtype=torch.bfloat16, device=dev)
-                ref_ms = []
+                # this layer's activations quantized at m rows, for the W4A4
+                # GEMM timed in the same loop as the bf16 product
+                qlin.quantize_nvfp4(r["x"][:m], codes=r["codes"][:m], scales=r["scales"][:m],
+                                    workspace=r["ws"], ts_out=r["ts"])
+                gws = r["gws"] if r["gws_bytes"][m] else None
+
+                def w4a4_gemm():
+                    qlin.gemm_w4a4(r["codes"][:m], r["scales"][:m], r["ts"], r["blob"], m, L.n,
+                                   L.k, y=r["y"][:m], workspace=gws)
+
+                ref_ms, w_ms = [], []
                 for _ in range(3):
                     torch.matmul(r["x"][:m], wb.t(), out=yb)
+                    w4a4_gemm()
                 torch.cuda.synchronize()
-                for _ in range(10):
+                for _ in range(10):   # alternating: the same clock and cache state for both
                     a, b = E(enable_timing=True), E(enable_timing=True)
                     a.record()
                     torch.matmul(r["x"][:m], wb.t(), out=yb)
                     b.record()
                     b.synchronize()
                     ref_ms.append(a.elapsed_time(b))
-                med = float(np.median(ref_ms))
+                    a, b = E(enable_timing=True), E(enable_timing=True)
+                    a.record()
+                    w4a4_gemm()
+                    b.record()
+                    b.synchronize()
+                    w_ms.append(a.elapsed_time(b))
+                med, wmed = float(np.median(ref_ms)), float(np.median(w_ms))
                 bf16_ref[f"prefill_{tag}/{L.name}"] = {
                     "us": round(med * 1e3, 1),
-                    "tflops": round(2.0 * m * L.n * L.k / med / 1e9, 1)}
+                    "tflops": round(2.0 * m * L.n * L.k / med / 1e9, 1),
+                    "w4a4_same_loop_us": round(wmed * 1e3, 1),
+                    "w4a4_same_loop_tflops": round(2.0 * m * L.n * L.k / wmed / 1e9, 1)}
+                tot_b, tot_w = tot_b + med, tot_w + wmed
                 del wb, yb
+            same_loop[f"{tag}_m{m}"] = round(tot_b / tot_w, 3)
         for d in D:
             L = d["L"]
             copies = [torch.randn((L.n, L.k), dtype=torch.bfloat16, device=dev)
@@ -795,6 +818,7 @@ def main():
             "w4a4_gemm_speedup_vs_bf16_qwen3_m8192": (
                 speedup("qwen3", sum(l["gemm_us"] for l in qwen["m8192"]["layers"]))
                 if "m8192" in qwen else None),
+            "w4a4_gemm_speedup_vs_bf16_same_loop": same_loop,
             "w4a16_gbps_mean_over_layers": _agg("w4a16", dec.ms),
             "lut2_gbps_mean_over_layers": _agg("lut2", lut.ms),
             "w4a16_sp24_gbps_mean_over_layers": _agg("w4a16_sp24", dec.ms),
