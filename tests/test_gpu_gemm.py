@@ -80,11 +80,16 @@ def test_w4a4_ragged(m, n, k):
     say("w4a4 ragged", m, n, k)
     blob = _nvfp4_blob(q, w)
     ac, as_, at = q.quantize_nvfp4(dev_f32(x))
+    ys = {}
     for dt in (torch.float32, torch.bfloat16):
-        y = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=dt)
+        y = ys[dt] = q.gemm_w4a4(ac, as_, at, blob, m, n, k, out_dtype=dt)
         torch.cuda.synchronize()
         ref = gemm.w4a4(*nvfp4.quantize(x), *nvfp4.quantize(w))
         _check(host_f64(y), ref, dt == torch.bfloat16)
+    # the bf16 epilogue (tiles staged through LDS, stored as whole rows) puts
+    # every element where the fp32 one does: the whole bf16 output is the
+    # round-to-nearest-even of the same kernel's fp32 output
+    assert torch.equal(ys[torch.bfloat16], ys[torch.float32].to(torch.bfloat16))
 
 
 # Batches of up to 32 tokens take the small-batch kernel (waves split k, one
@@ -509,6 +514,9 @@ def test_w4a4_cooperative_ragged_edges(m, n, k):
                     *nvfp4.quantize(w[cols], s_t=nvfp4.tensor_scale(w)))
     _check(host_f64(y32)[np.ix_(rows, cols)], ref, False)
     _check(host_f64(y16)[np.ix_(rows, cols)], ref, True)
+    # the whole bf16 output (staged through LDS per wave, stored as whole rows)
+    # is the round-to-nearest-even of the fp32 output of the same kernel
+    assert torch.equal(y16, y32.to(torch.bfloat16))
     # nothing was written past the output: the buffers are exactly [m, n]
     assert y32.shape == (m, n) and y16.shape == (m, n)
 
