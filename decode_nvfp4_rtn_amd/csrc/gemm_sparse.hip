@@ -185,7 +185,9 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
   // waits for): tested once here, for every store below
   const bool hdr_ok = header_word_ok(hdr, 3, N, K);
 
-  __shared__ float red[2][KW][MT][4][64];
+  // 65-float rows with one m-tile: the row-wise final sums below read them
+  // free of bank conflicts
+  __shared__ float red[2][KW][MT][4][MT == 1 ? 65 : 64];
   auto finish = [&](const Tile& A, int t, int slot, bool store) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -201,16 +203,23 @@ void sp24_persist_kernel(const uint16_t* __restrict__ x, const uint8_t* __restri
     }
     __syncthreads();
     // (a blob of another format or shape is read but never stored from)
+    // One m-tile: wave rq adds token rows 4 rq .. 4 rq + 3, all 16 columns,
+    // so each store writes whole 32-byte row pieces (accumulator lane row +
+    // 16 (column / 4), component column % 4, held that output), as in the
+    // dense persistent kernel; two m-tiles keep one component per wave.
     if (wave < 4 * MT && store && hdr_ok) {
-      const int mt = wave >> 2, r = wave & 3;
+      const int mt = wave >> 2;
+      const int mrow = MT == 1 ? 4 * (wave & 3) + (lane >> 4) : (lane & 15);
+      const int col = MT == 1 ? (lane & 15) : 4 * (lane >> 4) + (wave & 3);
+      const int r = col & 3, src = mrow + 16 * (col >> 2);
       float v[KW];
 #pragma unroll
-      for (int w = 0; w < KW; ++w) v[w] = red[slot][w][mt][r][lane];
+      for (int w = 0; w < KW; ++w) v[w] = red[slot][w][mt][r][src];
 #pragma unroll
       for (int h = KW / 2; h >= 1; h /= 2)
 #pragma unroll
         for (int w = 0; w < h; ++w) v[w] += v[w + h];
-      const int m = mt * 16 + (lane & 15), n = t * 16 + 4 * (lane >> 4) + r;
+      const int m = mt * 16 + mrow, n = t * 16 + col;
       if (m < M) {
         if (S > 1)
           part[(int64_t(sl) * M + m) * N + n] = v[0];   // this slice's partial sum
